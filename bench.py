@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Throughput of the SwiGLU backward hot path on one MI355X.
+
+One step = the three SwiGLU backward stages at the large-batch FFN shape of the Fused
+SwiGLU backward page (M=220000 tokens, K=512, N=1024, bf16: b stage with the db column
+sums, w-stage GEMM, x-stage GEMM) followed by the beta-scaled Swish gradient over
+L = 2^24 + 37 elements in fp32, fp16 and bf16 (beta = 1.702).  Inputs are synthetic
+(seeded), resident in HBM before timing starts.
+
+Reported value: the step's fraction of its roofline, 100 * sum(roofline time of each
+stage) / (measured step time), where a stage's roofline time is its algorithmic bytes
+over 8 TB/s (HBM) or its flops over 2.5 PFLOP/s (dense bf16 MFMA), whichever is larger.
+Each stage's absolute GB/s or TFLOP/s is listed too.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SwiGLU-bwd GB/s (b kernel) + TFLOP/s (w/x GEMMs), % of roofline"
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, MI355X dense bf16 matrix cores
+SWISH_BETA = 1.702
+SWISH_DTYPES = ("fp32", "fp16", "bf16")
+ES = {"fp32": 4, "fp16": 2, "bf16": 2}
+
+KERNELS = {
+    "b": ["b_stage_kernel", "db_finalize_kernel"],
+    "w": ["w_stage_kernel", "w_reduce_kernel"],
+    "x": ["x_stage_kernel"],
+    "swish_grad": ["swish_grad_vec_kernel"],
+}
+
+
+def stage_work(M, K, N, L):
+    """Algorithmic bytes and flops per stage (extra traffic of partial sums excluded)."""
+    w = {
+        "b": {"bytes": 10 * M * N + 8 * N, "flops": 0},
+        "w": {"bytes": 2 * M * K + 4 * M * N + 8 * K * N, "flops": 4 * M * K * N},
+        "x": {"bytes": 4 * M * N + 4 * K * N + 2 * M * K, "flops": 4 * M * K * N},
+    }
+    for dt in SWISH_DTYPES:
+        w[f"swish_grad_{dt}"] = {"bytes": 3 * ES[dt] * L, "flops": 0}
+    for v in w.values():
+        t_mem = v["bytes"] / HBM_PEAK
+        t_mma = v["flops"] / MFMA_BF16_PEAK
+        v["bound"] = "mfma" if t_mma > t_mem else "hbm"
+        v["t_roof"] = max(t_mem, t_mma)
+    return w
+
+
+def cpu_baseline(inp, sw_inputs, rows, swish_len):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle.ref as R
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                            if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = len(os.sched_getaffinity(0))
+    f64 = lambda t: t.double().numpy()  # noqa: E731
+    M, N = inp["dy"].shape
+    K = inp["x"].shape[1]
+    m = min(rows, M)
+    dy, g, fc, x = (f64(inp[k][:m]) for k in ("dy", "g", "fc", "x"))
+    wg, wf = f64(inp["w_g"]), f64(inp["w_fc"])
+    sw = {dt: (f64(v["grad"][:swish_len]), f64(v["x"][:swish_len])) for dt, v in sw_inputs.items()}
+    t0 = time.perf_counter()
+    dg, dfc, _, _ = R.b_ref(dy, g, fc)
+    R.w_ref(x, dg, dfc)
+    R.x_ref(dg, dfc, wg, wf)
+    for dt in SWISH_DTYPES:
+        R.swish_grad_ref(sw[dt][0], sw[dt][1], SWISH_BETA)
+    t = time.perf_counter() - t0
+    work = stage_work(m, K, N, swish_len)
+    t_roof = sum(v["t_roof"] for v in work.values())
+    return {"value": round(100.0 * t_roof / t, 6), "unit": "% of roofline",
+            "cores": int(blas_threads), "kind": "oracle",
+            "seconds": round(t, 3),
+            "sample": f"first {m} of {M} rows (b, w, x stages) and first {swish_len} elements "
+                      f"of the Swish input per dtype; numpy float64, element-wise work on 1 "
+                      f"thread, GEMMs on {blas_threads} BLAS threads",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ffn_220k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=49152)
+    ap.add_argument("--cpu-swish-len", type=int, default=1 << 22)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the data-parallel "
+              "split over M and its all-reduce of db/dw are design notes only); run with "
+              "--gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import swish_activation_backward_amd as swg
+    from workloads.gen import SWIGLU_WORKLOADS, SWISH_WORKLOAD, swiglu_inputs, swish_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    swg.load_library()
+    dev = torch.device("cuda", 0)
+    shape = SWIGLU_WORKLOADS[args.workload]
+    M, K, N = shape.M, shape.K, shape.N
+    L = SWISH_WORKLOAD["L"]
+
+    inp = swiglu_inputs(shape)
+    sw_inputs = {dt: swish_inputs(dt) for dt in SWISH_DTYPES}
+    d = {k: v.to(dev) for k, v in inp.items()}
+    sw = {dt: {k: v.to(dev) for k, v in s.items()} for dt, s in sw_inputs.items()}
+    sw_out = {dt: torch.empty_like(sw[dt]["grad"]) for dt in SWISH_DTYPES}
+    dg, dfc = torch.empty_like(d["dy"]), torch.empty_like(d["dy"])
+    db_g = torch.zeros(N, dtype=torch.bfloat16, device=dev)
+    db_fc = torch.zeros_like(db_g)
+    dw_g = torch.zeros(K, N, dtype=torch.bfloat16, device=dev)
+    dw_fc = torch.zeros_like(dw_g)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    ws_b = torch.empty(max(1, swg.swiglu_bwd_b_workspace_size(M, N, torch.bfloat16)),
+                       dtype=torch.uint8, device=dev)
+    ws_w = torch.empty(max(1, swg.swiglu_bwd_w_workspace_size(M, K, N, torch.bfloat16)),
+                       dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    names = ["b", "w", "x"] + [f"swish_grad_{dt}" for dt in SWISH_DTYPES]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        swg.swiglu_bwd_b(d["dy"], d["g"], d["fc"], dg, dfc, db_g, db_fc, workspace=ws_b)
+        if ev is not None:
+            ev[1].record(stream)
+        swg.swiglu_bwd_w(d["x"], dg, dfc, dw_g, dw_fc, workspace=ws_w)
+        if ev is not None:
+            ev[2].record(stream)
+        swg.swiglu_bwd_x(dg, dfc, d["w_g"], d["w_fc"], dx)
+        if ev is not None:
+            ev[3].record(stream)
+        for i, dt in enumerate(SWISH_DTYPES):
+            swg.swish_grad(sw[dt]["grad"], sw[dt]["x"], grad_x=sw_out[dt], beta=SWISH_BETA)
+            if ev is not None:
+                ev[4 + i].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_stage = {n: 0.0 for n in names}
+    for ev in events:
+        for i, n in enumerate(names):
+            per_stage[n] += ev[i].elapsed_time(ev[i + 1]) * 1e-3
+    per_stage = {n: v / args.steps for n, v in per_stage.items()}
+    step_s = sum(per_stage.values())
+    work = stage_work(M, K, N, L)
+    t_roof = sum(v["t_roof"] for v in work.values())
+
+    stages = {}
+    for n in names:
+        t = per_stage[n]
+        wk = work[n]
+        e = {"us": round(t * 1e6, 2), "GB/s": round(wk["bytes"] / t / 1e9, 1),
+             "bound": wk["bound"], "roofline_us": round(wk["t_roof"] * 1e6, 2),
+             "frac": round(wk["t_roof"] / t, 4),
+             "kernels": KERNELS["swish_grad" if n.startswith("swish") else n]}
+        if wk["flops"]:
+            e["TFLOP/s"] = round(wk["flops"] / t / 1e12, 1)
+        stages[n] = e
+    dom = max(names, key=lambda n: per_stage[n])
+    wk, t = work[dom], per_stage[dom]
+    if wk["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": round(wk["flops"] / t / 1e12, 2),
+                "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(wk["bytes"] / t / 1e9, 1),
+                "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["stage"] = dom
+    roof["kernels"] = stages[dom]["kernels"]
+    roof["avg_launch_us"] = stages[dom]["us"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(100.0 * t_roof / step_s, 3),
+        "unit": "% of roofline",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"swiglu_bwd {shape.name} M={M} K={K} N={N} bf16 + swish_grad "
+                               f"L={L} fp32/fp16/bf16 beta={SWISH_BETA}",
+                   "M": M, "K": K, "N": N, "swish_L": L, "parallelism": "single GPU"},
+        "event_ms_per_step": round(step_s * 1e3, 4),
+        "roofline_ms_per_step": round(t_roof * 1e3, 4),
+        "stages": stages,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, sw_inputs, args.cpu_rows, args.cpu_swish_len)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

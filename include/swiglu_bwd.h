@@ -1,0 +1,132 @@
+/*
+ * swiglu_bwd.h — C ABI of the MI355X (gfx950) SwiGLU backward and Swish-gradient library.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [SwiGLU page]  "PyPTO-Gym 实战: Fused SwiGLU 反向传播算子 (Ascend NPU 三 Kernel 融合实现)",
+ *                  sections "算法概述与数学公式" (formulas 1-4), "Kernel 概览与调用链" (call
+ *                  chain b -> w -> x), "Kernel 签名与参数规格" (shapes, dtypes, zero-init
+ *                  accumulators), "动态轴" (dynamic M), "Dtype 转换流程" (bf16 storage,
+ *                  fp32 arithmetic).
+ *   [Swish page]   "CANN ops-nn 中 SwishGrad 算子解析: 原理、实现与 aclnnSwishBackward 调用指南",
+ *                  sections 1.2 (formula), 1.3 (parameters, optional scale = beta, default 1.0),
+ *                  2.4 (fp16/bf16 widened to fp32, rounded back to nearest even),
+ *                  3.3 / 3.5 (argument checks, empty tensors return success with no work).
+ *
+ * Conventions shared by every call:
+ *   - All tensors are dense, row-major, contiguous device buffers (hipMalloc'd or any
+ *     device-accessible pointer).  The library never allocates, frees or copies device
+ *     memory and never synchronises; every call only validates its arguments on the host
+ *     and enqueues kernels on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Sizes are int64_t element counts.  The batch size M (and the Swish length n) is a
+ *     run-time argument of any value >= 0: there is no per-size compilation and the last
+ *     partial tile is masked, never padded.
+ *   - Arithmetic is fp32; results are rounded once to the storage dtype with
+ *     round-to-nearest-even.
+ *   - Every pointer must be aligned to its element size.  Buffers may not overlap unless
+ *     a call says otherwise.
+ *   - Errors are reported before anything is enqueued: SWG_ERR_NULLPTR for a NULL
+ *     pointer that the call would touch, SWG_ERR_INVALID for a negative size, an unknown
+ *     dtype or a misaligned pointer, SWG_ERR_UNSUPPORTED for a dtype/shape combination
+ *     the call does not implement, SWG_ERR_WORKSPACE for a workspace smaller than the
+ *     matching *_workspace_size query.  SWG_ERR_HIP means a launch failed; the HIP error
+ *     code is then available from swg_last_hip_error().  Calls whose work is empty return
+ *     SWG_OK without launching anything.
+ *   - Calls are thread-safe: the library keeps no state apart from the last HIP error.
+ */
+#ifndef SWIGLU_BWD_H
+#define SWIGLU_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SWG_BF16 = 0, SWG_FP16 = 1, SWG_FP32 = 2 } swg_dtype;
+
+typedef enum {
+  SWG_OK = 0,
+  SWG_ERR_NULLPTR = 1,
+  SWG_ERR_INVALID = 2,
+  SWG_ERR_UNSUPPORTED = 3,
+  SWG_ERR_WORKSPACE = 4,
+  SWG_ERR_HIP = 5
+} swg_status;
+
+/*
+ * b stage [SwiGLU page, formulas 1 and 2; kernel 1 of the call chain]:
+ *   s = sigma(g) = 1 / (1 + exp(-g))
+ *   dg[m,n]  = dy[m,n] * fc[m,n] * s * (1 + g[m,n] * (1 - s))
+ *   dfc[m,n] = dy[m,n] * g[m,n] * s
+ *   db_g[n]  = RNE(db_g[n]  + sum_m dg[m,n])     (accumulated, see below)
+ *   db_fc[n] = RNE(db_fc[n] + sum_m dfc[m,n])
+ * dy, g, fc, dg, dfc: [M, N]; db_g, db_fc: [N] (the page's [1, N]).  dtype: bf16, fp16
+ * or fp32, the same for every tensor.  dg and dfc are overwritten.  db_g and db_fc are
+ * ACCUMULATED: the column sums are formed from the fp32 values of dg/dfc (before their
+ * rounding), in a fixed order (run-to-run deterministic, no atomics), added to the
+ * current contents and rounded once; the caller zeroes them for a plain gradient.
+ * `workspace` must hold swiglu_bwd_b_workspace_size(M, N, dtype) bytes of device memory
+ * (fp32 column partials; contents on entry are ignored, contents on return unspecified);
+ * it may be NULL when that size is 0.  No aliasing between any two buffers.
+ */
+swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc,
+                        void* dg, void* dfc, void* db_g, void* db_fc,
+                        int64_t M, int64_t N, swg_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+size_t swiglu_bwd_b_workspace_size(int64_t M, int64_t N, swg_dtype dtype);
+
+/*
+ * w stage [SwiGLU page, formula 3; kernel 2]:  [dw_g | dw_fc] += x^T [dg | dfc]
+ * one GEMM [K, M] x [M, 2N] whose right operand is the column concatenation of dg and dfc.
+ *   dw_g[k,n]  = RNE(dw_g[k,n]  + sum_m x[m,k] * dg[m,n])
+ *   dw_fc[k,n] = RNE(dw_fc[k,n] + sum_m x[m,k] * dfc[m,n])
+ * x: [M, K]; dg, dfc: [M, N]; dw_g, dw_fc: [K, N].  dtype: bf16 or fp16 (fp32 returns
+ * SWG_ERR_UNSUPPORTED).  K and N must be multiples of 8 (16-byte rows), otherwise
+ * SWG_ERR_UNSUPPORTED.  Products are formed on the matrix cores, accumulated in fp32
+ * (split over M in fixed-order fp32 partials when the output is small), added to the
+ * current dw and rounded once: dw is ACCUMULATED like db.  `workspace` holds
+ * swiglu_bwd_w_workspace_size(M, K, N, dtype) bytes (0 when no split is needed).
+ */
+swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc,
+                        void* dw_g, void* dw_fc,
+                        int64_t M, int64_t K, int64_t N, swg_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+size_t swiglu_bwd_w_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dtype);
+
+/*
+ * x stage [SwiGLU page, formula 4; kernel 3]:  dx = [dg | dfc] [W_g | W_fc]^T
+ * one GEMM [M, 2N] x [2N, K]:  dx[m,k] = sum_n dg[m,n] W_g[k,n] + dfc[m,n] W_fc[k,n].
+ * dg, dfc: [M, N]; w_g, w_fc: [K, N] (row-major, as on the page); dx: [M, K], OVERWRITTEN.
+ * dtype: bf16 or fp16; K and N multiples of 8 (else SWG_ERR_UNSUPPORTED).  fp32
+ * accumulation, one rounding.  N = 0 with M*K > 0 writes dx = 0 (the empty sum).
+ */
+swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
+                        void* dx, int64_t M, int64_t K, int64_t N, swg_dtype dtype,
+                        void* stream);
+
+/*
+ * Swish gradient with a scalar beta [Swish page, sections 1.2 and 2.4]:
+ *   t = beta * x,  s = sigma(t),  grad_x = grad * s * (1 + t * (1 - s))
+ * grad, x, grad_x: n elements of one dtype (bf16, fp16 or fp32).  `beta` points to a
+ * host float; NULL means 1.0 (the page's default when the scale is absent).  Any finite
+ * beta is valid (beta = 0 gives grad / 2).  grad_x may alias grad or x exactly (in-place);
+ * no other overlap is allowed.
+ */
+swg_status swish_grad(const void* grad, const void* x, void* grad_x, int64_t n,
+                      swg_dtype dtype, const float* beta, void* stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* swg_status_string(int status);
+
+/* The hipError_t of the most recent SWG_ERR_HIP on the calling thread (0 if none). */
+int swg_last_hip_error(void);
+
+/* Library version, e.g. "swiglu_bwd 0.1.0 gfx950". */
+const char* swg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_BWD_H */

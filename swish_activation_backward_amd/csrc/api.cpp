@@ -1,0 +1,143 @@
+// C ABI of the SwiGLU backward / Swish-gradient library: argument validation, launch
+// planning and dispatch.  Every check happens on the host before anything is enqueued;
+// the rules follow the SwishGrad page's aclnn interface (section 3.3: NULL tensors ->
+// null-pointer error, bad dtype or shape -> invalid-parameter error; section 3.5:
+// empty tensors return success without running anything; a missing beta means 1.0)
+// and the Fused SwiGLU backward page's kernel signatures (section "Kernel 签名与参数规格").
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/swiglu_bwd.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+using namespace swg;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool dtype_ok(int dt) { return dt == SWG_BF16 || dt == SWG_FP16 || dt == SWG_FP32; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+swg_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return SWG_OK;
+  g_last_hip_error = (int)e;
+  return SWG_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* swg_version(void) { return "swiglu_bwd 0.1.0 gfx950"; }
+
+const char* swg_status_string(int status) {
+  switch (status) {
+    case SWG_OK: return "SWG_OK";
+    case SWG_ERR_NULLPTR: return "SWG_ERR_NULLPTR: a required pointer is NULL";
+    case SWG_ERR_INVALID: return "SWG_ERR_INVALID: negative size, unknown dtype or misaligned pointer";
+    case SWG_ERR_UNSUPPORTED: return "SWG_ERR_UNSUPPORTED: dtype or shape not implemented by this call";
+    case SWG_ERR_WORKSPACE: return "SWG_ERR_WORKSPACE: workspace smaller than the size query";
+    case SWG_ERR_HIP: return "SWG_ERR_HIP: a HIP launch failed (see swg_last_hip_error)";
+    default: return "unknown swg_status";
+  }
+}
+
+int swg_last_hip_error(void) { return g_last_hip_error; }
+
+// ------------------------------------------------------------------- swish_grad
+swg_status swish_grad(const void* grad, const void* x, void* grad_x, int64_t n, swg_dtype dtype,
+                      const float* beta, void* stream) {
+  if (!dtype_ok(dtype) || n < 0) return SWG_ERR_INVALID;
+  if (n == 0) return SWG_OK;
+  if (grad == nullptr || x == nullptr || grad_x == nullptr) return SWG_ERR_NULLPTR;
+  const size_t es = (size_t)elem_size(dtype);
+  if (!aligned(grad, es) || !aligned(x, es) || !aligned(grad_x, es)) return SWG_ERR_INVALID;
+  // only exact aliasing of the output with an input is allowed
+  const uintptr_t o = reinterpret_cast<uintptr_t>(grad_x);
+  const uintptr_t bytes = (uintptr_t)n * es;
+  for (const void* in : {grad, x}) {
+    const uintptr_t i = reinterpret_cast<uintptr_t>(in);
+    if (i != o && i < o + bytes && o < i + bytes) return SWG_ERR_INVALID;
+  }
+  const float b = beta ? *beta : 1.0f;
+  const bool vec = aligned(grad, 16) && aligned(x, 16) && aligned(grad_x, 16);
+  return hip_status(launch_swish_grad(dtype, grad, x, grad_x, n, b, vec, as_stream(stream)));
+}
+
+// ------------------------------------------------------------------- b stage
+size_t swiglu_bwd_b_workspace_size(int64_t M, int64_t N, swg_dtype dtype) {
+  if (!dtype_ok(dtype) || M <= 0 || N <= 0) return 0;
+  return plan_b(M, N, dtype, true).ws_bytes;
+}
+
+swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc, void* dg, void* dfc,
+                        void* db_g, void* db_fc, int64_t M, int64_t N, swg_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || M < 0 || N < 0) return SWG_ERR_INVALID;
+  if (M == 0 || N == 0) return SWG_OK;  // dg/dfc empty; db += empty sum
+  if (!dy || !g || !fc || !dg || !dfc || !db_g || !db_fc) return SWG_ERR_NULLPTR;
+  const size_t es = (size_t)elem_size(dtype);
+  for (const void* p : {dy, g, fc, (const void*)dg, (const void*)dfc, (const void*)db_g,
+                        (const void*)db_fc})
+    if (!aligned(p, es)) return SWG_ERR_INVALID;
+  const bool vec = aligned(dy, 16) && aligned(g, 16) && aligned(fc, 16) && aligned(dg, 16) &&
+                   aligned(dfc, 16);
+  const BPlan p = plan_b(M, N, dtype, vec);
+  if (workspace_bytes < p.ws_bytes) return SWG_ERR_WORKSPACE;
+  if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
+  if (!aligned(workspace, 16)) return SWG_ERR_INVALID;
+  return hip_status(launch_b_stage(dtype, p, dy, g, fc, dg, dfc, db_g, db_fc, M, N,
+                                   static_cast<float*>(workspace), as_stream(stream)));
+}
+
+// ------------------------------------------------------------------- GEMM stages
+static swg_status gemm_shape_check(int dtype, int64_t M, int64_t K, int64_t N) {
+  if (!dtype_ok(dtype) || M < 0 || K < 0 || N < 0) return SWG_ERR_INVALID;
+  if (dtype == SWG_FP32) return SWG_ERR_UNSUPPORTED;
+  if (K % 8 != 0 || N % 8 != 0) return SWG_ERR_UNSUPPORTED;
+  return SWG_OK;
+}
+
+size_t swiglu_bwd_w_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dtype) {
+  if (gemm_shape_check(dtype, M, K, N) != SWG_OK || M == 0 || K == 0 || N == 0) return 0;
+  return plan_w(M, K, N).ws_bytes;
+}
+
+swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc, void* dw_g, void* dw_fc,
+                        int64_t M, int64_t K, int64_t N, swg_dtype dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  swg_status st = gemm_shape_check(dtype, M, K, N);
+  if (st != SWG_OK) return st;
+  if (M == 0 || K == 0 || N == 0) return SWG_OK;  // dw += empty sum
+  if (!x || !dg || !dfc || !dw_g || !dw_fc) return SWG_ERR_NULLPTR;
+  for (const void* p : {x, dg, dfc}) if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
+  for (const void* p : {(const void*)dw_g, (const void*)dw_fc}) if (!aligned(p, 8)) return SWG_ERR_UNSUPPORTED;
+  const WPlan p = plan_w(M, K, N);
+  if (workspace_bytes < p.ws_bytes) return SWG_ERR_WORKSPACE;
+  if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
+  if (!aligned(workspace, 16)) return SWG_ERR_INVALID;
+  return hip_status(launch_w_stage(dtype, p, x, dg, dfc, dw_g, dw_fc, M, K, N,
+                                   static_cast<float*>(workspace), as_stream(stream)));
+}
+
+swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
+                        void* dx, int64_t M, int64_t K, int64_t N, swg_dtype dtype, void* stream) {
+  swg_status st = gemm_shape_check(dtype, M, K, N);
+  if (st != SWG_OK) return st;
+  if (M == 0 || K == 0) return SWG_OK;  // dx is empty
+  if (!dx) return SWG_ERR_NULLPTR;
+  if (!aligned(dx, 16)) return SWG_ERR_UNSUPPORTED;
+  if (N == 0)  // the empty sum: dx = 0
+    return hip_status(launch_zero(dx, (size_t)M * (size_t)K * 2, as_stream(stream)));
+  if (!dg || !dfc || !w_g || !w_fc) return SWG_ERR_NULLPTR;
+  for (const void* p : {dg, dfc, w_g, w_fc}) if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
+  return hip_status(launch_x_stage(dtype, dg, dfc, w_g, w_fc, dx, M, K, N, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Internal launchers (C++ linkage) called by the C ABI layer after validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace swg {
+
+constexpr int64_t kMaxStreamBlocks = 8192;
+
+hipError_t launch_swish_grad(int dtype, const void* grad, const void* x, void* out, int64_t n,
+                             float beta, bool vector_path, hipStream_t stream);
+
+hipError_t launch_b_stage(int dtype, const BPlan& p, const void* dy, const void* g,
+                          const void* fc, void* dg, void* dfc, void* db_g, void* db_fc,
+                          int64_t M, int64_t N, float* part, hipStream_t stream);
+
+hipError_t launch_w_stage(int dtype, const WPlan& p, const void* x, const void* dg,
+                          const void* dfc, void* dw_g, void* dw_fc, int64_t M, int64_t K,
+                          int64_t N, float* ws, hipStream_t stream);
+
+hipError_t launch_x_stage(int dtype, const void* dg, const void* dfc, const void* w_g,
+                          const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N,
+                          hipStream_t stream);
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+
+}  // namespace swg

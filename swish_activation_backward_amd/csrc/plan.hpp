@@ -1,0 +1,97 @@
+// Host-side launch planning, shared by the workspace-size queries and the launches so
+// the two always agree.  Pure integer arithmetic: no HIP calls.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swg {
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int elem_size(int dtype) { return dtype == 2 ? 4 : 2; }
+inline int vec_of(int dtype) { return 16 / elem_size(dtype); }
+
+// ---------------------------------------------------------------- b stage
+// A workgroup of 256 threads owns a strip of TX vector-columns (TX a power of two
+// <= 64) and a chunk of rows; TY = 256 / TX rows are in flight per step.  Each
+// chunk leaves one fp32 partial row [2N] (dg sums, then dfc sums) in the workspace,
+// which the finalize kernel sums in chunk order.
+struct BPlan {
+  int vec;             // elements per 16-byte access (1 when the scalar path is used)
+  int tx, ty;          // thread layout inside the 256-thread workgroup
+  int64_t cv;          // vector columns per row = N / vec
+  int64_t nstrips;     // ceil(cv / tx)
+  int64_t nchunks;     // row chunks (grid.y)
+  int64_t rows;        // rows per chunk
+  size_t ws_bytes;     // nchunks * 2N * sizeof(float)
+};
+
+constexpr int kBThreads = 256;
+constexpr int64_t kBTargetBlocks = 2048;
+constexpr int64_t kBMinRows = 32;
+
+inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
+  BPlan p{};
+  // the chunking depends only on (M, N, dtype), never on pointer alignment
+  const int vref = vec_of(dtype);
+  const int64_t cv_ref = (N % vref == 0) ? N / vref : N;
+  int tx_ref = 1;
+  while (tx_ref < 64 && tx_ref < cv_ref) tx_ref <<= 1;
+  const int64_t strips_ref = ceil_div(cv_ref, tx_ref);
+  int64_t nchunks = ceil_div(kBTargetBlocks, strips_ref);
+  const int64_t max_chunks = ceil_div(M, kBMinRows);
+  if (nchunks > max_chunks) nchunks = max_chunks;
+  if (nchunks < 1) nchunks = 1;
+  p.rows = ceil_div(M, nchunks);
+  p.nchunks = M > 0 ? ceil_div(M, p.rows) : 0;
+  p.ws_bytes = (M > 0 && N > 0) ? (size_t)p.nchunks * (size_t)(2 * N) * sizeof(float) : 0;
+
+  p.vec = (vector_path && N % vref == 0) ? vref : 1;
+  p.cv = N / p.vec;
+  int tx = 1;
+  while (tx < 64 && tx < p.cv) tx <<= 1;
+  p.tx = tx;
+  p.ty = kBThreads / tx;
+  p.nstrips = ceil_div(p.cv, tx);
+  return p;
+}
+
+// ---------------------------------------------------------------- GEMM tiles
+// Both GEMMs use 256 x 256 output tiles and a 64-deep contraction step per LDS stage.
+constexpr int kTileP = 256;     // output rows per workgroup
+constexpr int kTileQ = 256;     // output cols per workgroup
+constexpr int kTileR = 64;      // contraction depth per LDS stage
+
+// w stage: output [K, 2N]; when it has too few tiles to fill the chip the batch
+// dimension M is split into S ranges whose fp32 partials are summed in order.
+struct WPlan {
+  int64_t tk, tn, tiles;   // tile grid over [K, 2N]
+  int64_t splits;          // S
+  int64_t rows;            // rows of M per split (multiple of kTileR)
+  size_t ws_bytes;         // S > 1: S * K * 2N * sizeof(float)
+};
+
+constexpr int64_t kWTargetBlocks = 256;
+constexpr int64_t kWMinRowsPerSplit = 512;
+
+inline WPlan plan_w(int64_t M, int64_t K, int64_t N) {
+  WPlan p{};
+  p.tk = ceil_div(K, kTileP);
+  p.tn = ceil_div(2 * N, kTileQ);
+  p.tiles = p.tk * p.tn;
+  int64_t s = p.tiles > 0 ? ceil_div(kWTargetBlocks, p.tiles) : 1;
+  const int64_t smax = M / kWMinRowsPerSplit;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  p.rows = ceil_div(ceil_div(M, s), kTileR) * kTileR;
+  if (p.rows < kTileR) p.rows = kTileR;
+  p.splits = M > 0 ? ceil_div(M, p.rows) : 1;
+  if (p.splits < 1) p.splits = 1;
+  p.ws_bytes = (p.splits > 1 && K > 0 && N > 0)
+                   ? (size_t)p.splits * (size_t)K * (size_t)(2 * N) * sizeof(float)
+                   : 0;
+  return p;
+}
+
+}  // namespace swg

@@ -7,11 +7,14 @@ Three checks are applied to every output tensor:
    (bf16 machine epsilon) and atol = 1e-4 (section "精度校验", precision check).
    fp16 and fp32 results take rtol 1e-3 and 1e-5; because a rtol-only rule fails
    correct fp32-arithmetic kernels near the zero of s' and on fp16 subnormals, their
-   atol is the rounding model of a correct fp32 evaluation (``swish_abs_model``);
+   atol is the rounding model of a correct fp32 evaluation (``*_abs_model``);
 2. a per-element mixed bound |gpu - ref| <= rtol * |ref| + E, where E is the
    rounding model of the arithmetic that produced the value (fp32 math + one final
    rounding).  This binds where atol = 1e-4 exceeds the outputs themselves;
 3. a normwise bound ||gpu - ref||_2 <= nw * ||ref||_2.
+
+``Checker`` accumulates the three over chunks so that large tensors can be compared
+piecewise; ``compare`` is the one-shot form.
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ FP16_SUBNORMAL_HALF = 2.0 ** -25
 
 RTOL = {"bf16": BF16_RTOL, "fp16": FP16_RTOL, "fp32": FP32_RTOL}
 NORMWISE = {"bf16": 2.0 ** -7, "fp16": 2.0 ** -10, "fp32": 2.0 ** -20}
+TORCH_NAME = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}
 
 
 def to64(t) -> np.ndarray:
@@ -40,75 +44,103 @@ def _sig(t):
         return 1.0 / (1.0 + np.exp(-t))
 
 
+FP32_TINY = 2.0 ** -126   # smallest normal fp32: hardware exp may flush below it
+
+
 def swish_abs_model(grad, x, beta):
     """Absolute error of a correct fp32 evaluation of grad*s'(beta x):
-    8 * 2^-24 * |grad| * (sigma(t) + |t| sigma(t) (1 - sigma(t))), t = beta x."""
+    8 * 2^-24 * |grad| * (sigma(t) + |t| sigma(t) (1 - sigma(t))), t = beta x, plus
+    |grad| (1 + |t|) 2^-126 for an exp(-|t|) flushed to zero below the fp32 normals."""
     t = float(np.float32(1.0 if beta is None else beta)) * to64(x)
     s = _sig(t)
-    return 8.0 * U32 * np.abs(to64(grad)) * (s + np.abs(t) * s * (1.0 - s))
+    ag = np.abs(to64(grad))
+    return 8.0 * U32 * ag * (s + np.abs(t) * s * (1.0 - s)) + ag * (1.0 + np.abs(t)) * FP32_TINY
 
 
 def dg_abs_model(dy, g, fc):
     g = to64(g)
     s = _sig(g)
-    return 8.0 * U32 * np.abs(to64(dy) * to64(fc)) * (s + np.abs(g) * s * (1.0 - s))
+    a = np.abs(to64(dy) * to64(fc))
+    return 8.0 * U32 * a * (s + np.abs(g) * s * (1.0 - s)) + a * (1.0 + np.abs(g)) * FP32_TINY
 
 
 def dfc_abs_model(dy, g):
     g = to64(g)
-    return 8.0 * U32 * np.abs(to64(dy) * g * _sig(g))
+    a = np.abs(to64(dy) * g)
+    return 8.0 * U32 * a * _sig(g) + a * FP32_TINY
 
 
 def sum_abs_model(abs_sum):
     """fp32 accumulation of a sum whose magnitude sum is ``abs_sum``."""
-    return 2.0 ** -16 * abs_sum
+    return 2.0 ** -16 * np.asarray(abs_sum, dtype=np.float64)
 
 
 class ParityError(AssertionError):
     pass
 
 
-def compare(name, gpu, ref, dtype, *, model_abs=None, atol=None, rtol=None,
-            normwise=None, raise_on_fail=True):
-    """Apply the three checks; return a stats dict (and raise on failure)."""
-    g = to64(gpu)
-    r = to64(ref)
-    if g.shape != r.shape:
-        raise ParityError(f"{name}: shape {g.shape} != {r.shape}")
-    rtol = RTOL[dtype] if rtol is None else rtol
-    nw = NORMWISE[dtype] if normwise is None else normwise
-    if atol is None:
-        if dtype == "bf16":
+class Checker:
+    def __init__(self, name, dtype, *, rtol=None, atol=None, normwise=None):
+        self.name, self.dtype = name, dtype
+        self.rtol = RTOL[dtype] if rtol is None else rtol
+        self.atol = atol
+        self.nw = NORMWISE[dtype] if normwise is None else normwise
+        self.n = self.nonfinite = self.contract_fail = self.mixed_fail = 0
+        self.ss_ref = self.ss_err = 0.0
+        self.max_abs_err = 0.0
+        self.worst = None
+        self.worst_excess = -np.inf
+
+    def add(self, gpu, ref, model_abs=None):
+        g, r = to64(gpu), to64(ref)
+        if g.shape != r.shape:
+            raise ParityError(f"{self.name}: shape {g.shape} != {r.shape}")
+        err = np.abs(g - r)
+        absr = np.abs(r)
+        if self.atol is not None:
+            atol = self.atol
+        elif self.dtype == "bf16":
             atol = BF16_ATOL
         else:
             atol = 0.0 if model_abs is None else model_abs
-            if dtype == "fp16":
+            if self.dtype == "fp16":
                 atol = atol + FP16_SUBNORMAL_HALF
-    err = np.abs(g - r)
-    absr = np.abs(r)
-    stats = {"name": name, "n": int(r.size)}
-    bad_nonfinite = int((~np.isfinite(g)).sum())
-    stats["nonfinite"] = bad_nonfinite
-    contract_bad = err > atol + rtol * absr
-    stats["contract_fail"] = int(contract_bad.sum())
-    if model_abs is not None:
-        extra = FP16_SUBNORMAL_HALF if dtype == "fp16" else 0.0
-        mixed_bad = err > rtol * absr + model_abs + extra
-        stats["mixed_fail"] = int(mixed_bad.sum())
-    else:
-        stats["mixed_fail"] = 0
-    nr = float(np.sqrt(np.sum(r * r)))
-    ne = float(np.sqrt(np.sum(err * err)))
-    stats["normwise"] = ne / nr if nr > 0 else ne
-    normwise_bad = (ne > nw * nr) if nr > 0 else (ne > 0)
-    stats["normwise_fail"] = bool(normwise_bad)
-    stats["max_abs_err"] = float(err.max()) if err.size else 0.0
-    ok = (bad_nonfinite == 0 and stats["contract_fail"] == 0 and stats["mixed_fail"] == 0
-          and not normwise_bad)
-    stats["ok"] = ok
-    if raise_on_fail and not ok:
-        idx = int(np.argmax(err - rtol * absr)) if err.size else 0
-        raise ParityError(
-            f"{name}: {stats}; worst at flat index {idx}: gpu={g.flat[idx]!r} "
-            f"ref={r.flat[idx]!r}")
-    return stats
+        self.n += r.size
+        self.nonfinite += int((~np.isfinite(g)).sum())
+        self.contract_fail += int((err > atol + self.rtol * absr).sum())
+        if model_abs is not None:
+            extra = FP16_SUBNORMAL_HALF if self.dtype == "fp16" else 0.0
+            bound = self.rtol * absr + model_abs + extra
+            self.mixed_fail += int((err > bound).sum())
+        self.ss_ref += float(np.sum(r * r))
+        self.ss_err += float(np.sum(err * err))
+        if err.size:
+            self.max_abs_err = max(self.max_abs_err, float(err.max()))
+            ex = err - self.rtol * absr
+            i = int(np.argmax(ex))
+            if ex.flat[i] > self.worst_excess:
+                self.worst_excess = float(ex.flat[i])
+                self.worst = (float(g.flat[i]), float(r.flat[i]))
+        return self
+
+    def result(self, raise_on_fail=True):
+        nr, ne = np.sqrt(self.ss_ref), np.sqrt(self.ss_err)
+        normwise = ne / nr if nr > 0 else ne
+        normwise_bad = (ne > self.nw * nr) if nr > 0 else (ne > 0)
+        stats = {"name": self.name, "n": self.n, "nonfinite": self.nonfinite,
+                 "contract_fail": self.contract_fail, "mixed_fail": self.mixed_fail,
+                 "normwise": float(normwise), "normwise_fail": bool(normwise_bad),
+                 "max_abs_err": self.max_abs_err}
+        ok = (self.nonfinite == 0 and self.contract_fail == 0 and self.mixed_fail == 0
+              and not normwise_bad)
+        stats["ok"] = ok
+        if raise_on_fail and not ok:
+            raise ParityError(f"{self.name}: {stats}; worst (gpu, ref) = {self.worst}")
+        return stats
+
+
+def compare(name, gpu, ref, dtype, *, model_abs=None, atol=None, rtol=None,
+            normwise=None, raise_on_fail=True):
+    """Apply the three checks to one tensor; return a stats dict (raise on failure)."""
+    return Checker(name, dtype, rtol=rtol, atol=atol, normwise=normwise).add(
+        gpu, ref, model_abs).result(raise_on_fail)

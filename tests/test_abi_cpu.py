@@ -1,0 +1,166 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments on
+the host before any launch (CPU only: no call here reaches a kernel launch)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import swish_activation_backward_amd as swg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swiglu_bwd.h")
+
+OK, NULLPTR, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3, 4
+BF16, FP16, FP32 = 0, 1, 2
+# fake, suitably aligned device addresses: validation must reject before touching them
+P = ctypes.c_void_p(0x10000)
+Q = ctypes.c_void_p(0x20000)
+R = ctypes.c_void_p(0x30000)
+S = ctypes.c_void_p(0x40000)
+T = ctypes.c_void_p(0x50000)
+U = ctypes.c_void_p(0x60000)
+V = ctypes.c_void_p(0x70000)
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return swg.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"swiglu_bwd_b", "swiglu_bwd_w", "swiglu_bwd_x", "swish_grad"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/swiglu_bwd.h but not exported"
+
+
+def test_status_strings_and_version(lib):
+    for code in range(6):
+        s = lib.swg_status_string(code).decode()
+        assert s.startswith(swg.STATUS[code])
+    assert lib.swg_status_string(99).decode() == "unknown swg_status"
+    assert swg.swg_version().startswith("swiglu_bwd")
+    assert "gfx950" in swg.swg_version()
+    assert lib.swg_last_hip_error() == 0
+
+
+def test_swish_grad_argument_errors(lib):
+    beta = ctypes.byref(ctypes.c_float(1.0))
+    assert lib.swish_grad(P, Q, R, 0, BF16, beta, NULL) == OK          # empty: no work
+    assert lib.swish_grad(NULL, NULL, NULL, 0, BF16, None, NULL) == OK
+    assert lib.swish_grad(P, Q, R, -1, BF16, beta, NULL) == INVALID
+    assert lib.swish_grad(P, Q, R, 10, 7, beta, NULL) == INVALID       # unknown dtype
+    assert lib.swish_grad(NULL, Q, R, 10, BF16, beta, NULL) == NULLPTR
+    assert lib.swish_grad(P, NULL, R, 10, FP16, beta, NULL) == NULLPTR
+    assert lib.swish_grad(P, Q, NULL, 10, FP32, None, NULL) == NULLPTR
+    odd = ctypes.c_void_p(0x10001)
+    assert lib.swish_grad(odd, Q, R, 10, BF16, beta, NULL) == INVALID  # misaligned
+    assert lib.swish_grad(P, Q, ctypes.c_void_p(0x10002 + 0x4), 10, FP32, beta, NULL) == INVALID
+    # partial overlap of output and input is rejected; exact aliasing is allowed
+    assert lib.swish_grad(P, Q, ctypes.c_void_p(0x10000 + 8), 100, BF16, beta, NULL) == INVALID
+    assert lib.swish_grad(P, Q, ctypes.c_void_p(0x20000 - 8), 100, BF16, beta, NULL) == INVALID
+
+
+def test_b_stage_argument_errors(lib):
+    ws = swg.swiglu_bwd_b_workspace_size
+    import torch
+    M, N = 1000, 64
+    need = ws(M, N, torch.bfloat16)
+    assert need > 0
+    args = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                         (("dy", P), ("g", Q), ("fc", R), ("dg", S), ("dfc", T), ("dbg", U),
+                          ("dbfc", V), ("M", M), ("N", N), ("dt", BF16), ("w", P),
+                          ("wb", need), ("s", NULL))]
+    assert lib.swiglu_bwd_b(*args(M=0)) == OK
+    assert lib.swiglu_bwd_b(*args(N=0)) == OK
+    assert lib.swiglu_bwd_b(*args(M=0, dy=NULL, w=NULL, wb=0)) == OK
+    assert lib.swiglu_bwd_b(*args(M=-1)) == INVALID
+    assert lib.swiglu_bwd_b(*args(N=-5)) == INVALID
+    assert lib.swiglu_bwd_b(*args(dt=3)) == INVALID
+    for k in ("dy", "g", "fc", "dg", "dfc", "dbg", "dbfc"):
+        assert lib.swiglu_bwd_b(*args(**{k: NULL})) == NULLPTR, k
+    assert lib.swiglu_bwd_b(*args(wb=need - 1)) == WORKSPACE
+    assert lib.swiglu_bwd_b(*args(w=NULL)) == NULLPTR
+    assert lib.swiglu_bwd_b(*args(dbg=ctypes.c_void_p(0x60001))) == INVALID
+
+
+def test_gemm_argument_errors(lib):
+    import torch
+    M, K, N = 4096, 64, 128
+    need = swg.swiglu_bwd_w_workspace_size(M, K, N, torch.bfloat16)
+    wa = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                       (("x", P), ("dg", Q), ("dfc", R), ("dwg", S), ("dwfc", T), ("M", M),
+                        ("K", K), ("N", N), ("dt", BF16), ("w", U), ("wb", need), ("s", NULL))]
+    assert lib.swiglu_bwd_w(*wa(M=0)) == OK
+    assert lib.swiglu_bwd_w(*wa(K=0)) == OK
+    assert lib.swiglu_bwd_w(*wa(M=-1)) == INVALID
+    assert lib.swiglu_bwd_w(*wa(dt=FP32)) == UNSUPPORTED
+    assert lib.swiglu_bwd_w(*wa(dt=9)) == INVALID
+    assert lib.swiglu_bwd_w(*wa(K=60)) == UNSUPPORTED
+    assert lib.swiglu_bwd_w(*wa(N=100)) == UNSUPPORTED
+    for k in ("x", "dg", "dfc", "dwg", "dwfc"):
+        assert lib.swiglu_bwd_w(*wa(**{k: NULL})) == NULLPTR, k
+    if need > 0:
+        assert lib.swiglu_bwd_w(*wa(wb=need - 1)) == WORKSPACE
+        assert lib.swiglu_bwd_w(*wa(w=NULL)) == NULLPTR
+    xa = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                       (("dg", P), ("dfc", Q), ("wg", R), ("wfc", S), ("dx", T), ("M", M),
+                        ("K", K), ("N", N), ("dt", BF16), ("s", NULL))]
+    assert lib.swiglu_bwd_x(*xa(M=0)) == OK
+    assert lib.swiglu_bwd_x(*xa(K=0, dx=NULL)) == OK
+    assert lib.swiglu_bwd_x(*xa(K=-8)) == INVALID
+    assert lib.swiglu_bwd_x(*xa(dt=FP32)) == UNSUPPORTED
+    assert lib.swiglu_bwd_x(*xa(N=12)) == UNSUPPORTED
+    for k in ("dg", "dfc", "wg", "wfc", "dx"):
+        assert lib.swiglu_bwd_x(*xa(**{k: NULL})) == NULLPTR, k
+    assert lib.swiglu_bwd_x(*xa(N=0, dx=NULL)) == NULLPTR
+    assert lib.swiglu_bwd_x(*xa(dg=ctypes.c_void_p(0x10008))) == UNSUPPORTED
+
+
+def test_workspace_queries():
+    import torch
+    b = swg.swiglu_bwd_b_workspace_size
+    w = swg.swiglu_bwd_w_workspace_size
+    assert b(0, 128, torch.bfloat16) == 0 and b(128, 0, torch.bfloat16) == 0
+    assert w(0, 64, 128, torch.bfloat16) == 0
+    assert w(100, 64, 128, torch.float32) == 0            # unsupported -> 0
+    # b: one fp32 partial row [2N] per row chunk, a bounded number of chunks
+    for (M, N) in ((256, 128), (8191, 1024), (220000, 1024), (16384, 14336), (1, 8), (37, 13)):
+        nb = b(M, N, torch.bfloat16)
+        assert nb % (2 * N * 4) == 0 and 0 < nb // (2 * N * 4) <= max(M, 1)
+        assert nb // (2 * N * 4) <= 4096
+    # w: the split-M partials only when the output tile grid is small
+    assert w(16384, 4096, 14336, torch.bfloat16) == 0
+    s3 = w(220000, 512, 1024, torch.bfloat16)
+    assert s3 % (512 * 2048 * 4) == 0 and 2 <= s3 // (512 * 2048 * 4) <= 256
+    assert w(256, 64, 128, torch.bfloat16) == 0
+
+
+def test_binding_checks_shapes_without_gpu():
+    import torch
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        swg.swish_grad(x, torch.zeros(4, 9, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        swg.swiglu_bwd_x(x, x, torch.zeros(8, 8, dtype=torch.float16), x, x)
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The package must not import the oracle or any CPU implementation."""
+    pkg = os.path.join(ROOT, "swish_activation_backward_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("the oracle", ""), f
+                assert "numpy" not in text, f

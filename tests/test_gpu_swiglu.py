@@ -1,0 +1,204 @@
+"""GPU parity of the SwiGLU backward stages (through the C ABI) against the float64 oracle:
+the tiny and ragged-batch workloads in full, odd shapes, accumulation into non-zero
+buffers, the chained b -> w -> x path, determinism and guard bands."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.ref as R
+import swish_activation_backward_amd as swg
+from gpu_util import Guarded, device, note, oracle_b_chunked, oracle_w_chunked, oracle_x_rows, rne
+from parity import Checker, compare, sum_abs_model, to64
+from workloads.gen import DTYPES, SwiGLUShape, swiglu_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _b_case(inp, dt, db0=None):
+    dev = device()
+    M, N = inp["dy"].shape
+    tdt = DTYPES[dt]
+    dy, g, fc = (inp[k].to(dev) for k in ("dy", "g", "fc"))
+    dg, dfc = Guarded((M, N), tdt, dev), Guarded((M, N), tdt, dev)
+    init = torch.zeros(N, dtype=tdt) if db0 is None else db0
+    db_g, db_fc = Guarded((N,), tdt, dev, fill=init.to(dev)), Guarded((N,), tdt, dev, fill=(-init).to(dev))
+    note(f"b stage M={M} N={N} {dt} init={'zero' if db0 is None else 'nonzero'}")
+    swg.swiglu_bwd_b(dy, g, fc, dg.t, dfc.t, db_g.t, db_fc.t)
+    torch.cuda.synchronize()
+    for buf in (dg, dfc, db_g, db_fc):
+        buf.check()
+    res = oracle_b_chunked(inp["dy"], inp["g"], inp["fc"], init, -init,
+                           gpu=(dg.t.cpu(), dfc.t.cpu()), dtype=dt)
+    res["check_dg"].result()
+    res["check_dfc"].result()
+    compare("db_g", db_g.t.cpu(), res["db_g"], dt,
+            model_abs=sum_abs_model(res["abs_g"] + np.abs(to64(init))))
+    compare("db_fc", db_fc.t.cpu(), res["db_fc"], dt,
+            model_abs=sum_abs_model(res["abs_fc"] + np.abs(to64(init))))
+    return dg.t, dfc.t
+
+
+def _w_case(x, dg, dfc, dt, dw0=None):
+    dev = device()
+    M, K = x.shape
+    N = dg.shape[1]
+    tdt = DTYPES[dt]
+    init = torch.zeros(K, N, dtype=tdt) if dw0 is None else dw0
+    dw_g = Guarded((K, N), tdt, dev, fill=init.to(dev))
+    dw_fc = Guarded((K, N), tdt, dev, fill=(2 * init).to(dev))
+    note(f"w stage M={M} K={K} N={N} {dt} init={'zero' if dw0 is None else 'nonzero'}")
+    swg.swiglu_bwd_w(x.to(dev), dg.to(dev), dfc.to(dev), dw_g.t, dw_fc.t)
+    torch.cuda.synchronize()
+    dw_g.check()
+    dw_fc.check()
+    rg, rf, ag, af = oracle_w_chunked(x, dg, dfc)
+    i64 = to64(init)
+    compare("dw_g", dw_g.t.cpu(), rg + i64, dt, model_abs=sum_abs_model(ag + np.abs(i64)))
+    compare("dw_fc", dw_fc.t.cpu(), rf + 2 * i64, dt, model_abs=sum_abs_model(af + 2 * np.abs(i64)))
+    return dw_g.t, dw_fc.t
+
+
+def _x_case(dg, dfc, w_g, w_fc, dt):
+    dev = device()
+    M, N = dg.shape
+    K = w_g.shape[0]
+    dx = Guarded((M, K), DTYPES[dt], dev)
+    note(f"x stage M={M} K={K} N={N} {dt}")
+    swg.swiglu_bwd_x(dg.to(dev), dfc.to(dev), w_g.to(dev), w_fc.to(dev), dx.t)
+    torch.cuda.synchronize()
+    dx.check()
+    ref, a = oracle_x_rows(dg, dfc, w_g, w_fc, slice(None))
+    compare("dx", dx.t.cpu(), ref, dt, model_abs=sum_abs_model(a))
+    return dx.t
+
+
+def _oracle_dg(inp, dt):
+    res = oracle_b_chunked(inp["dy"], inp["g"], inp["fc"], store_dtype=DTYPES[dt])
+    return res["dg"], res["dfc"]
+
+
+@pytest.mark.parametrize("wl", ["tiny", "ragged"])
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+def test_b_stage_workloads(wl, dt):
+    inp = swiglu_inputs(wl, dtype=dt)
+    _b_case(inp, dt)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_b_stage_accumulates_into_nonzero_db(dt):
+    inp = swiglu_inputs("ragged", dtype=dt)
+    N = inp["dy"].shape[1]
+    db0 = (torch.randn(N, generator=torch.Generator().manual_seed(5)) * 0.05).to(DTYPES[dt])
+    _b_case(inp, dt, db0=db0)
+
+
+@pytest.mark.parametrize("M,N", [(1, 1), (37, 13), (300, 8), (129, 1000), (2, 2056),
+                                 (4097, 24), (5, 4104), (70000, 16)])
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_b_stage_odd_shapes(M, N, dt):
+    inp = swiglu_inputs(SwiGLUShape("odd", 11, M, 8, N), dtype=dt)
+    _b_case(inp, dt)
+
+
+def test_b_stage_unaligned_rows_use_scalar_path():
+    """N = 12: rows are not 16-byte aligned, so the element-wise path runs."""
+    inp = swiglu_inputs(SwiGLUShape("odd", 12, 999, 8, 12), dtype="bf16")
+    _b_case(inp, "bf16")
+
+
+@pytest.mark.parametrize("wl", ["tiny", "ragged"])
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_w_stage_workloads(wl, dt):
+    inp = swiglu_inputs(wl, dtype=dt)
+    dg, dfc = _oracle_dg(inp, dt)
+    _w_case(inp["x"], dg, dfc, dt)
+
+
+def test_w_stage_accumulates_into_nonzero_dw():
+    inp = swiglu_inputs("ragged", dtype="bf16")
+    dg, dfc = _oracle_dg(inp, "bf16")
+    K, N = inp["w_g"].shape
+    dw0 = (torch.randn(K, N, generator=torch.Generator().manual_seed(8)) * 1e-3).to(torch.bfloat16)
+    _w_case(inp["x"], dg, dfc, "bf16", dw0=dw0)
+
+
+@pytest.mark.parametrize("wl", ["tiny", "ragged"])
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_x_stage_workloads(wl, dt):
+    inp = swiglu_inputs(wl, dtype=dt)
+    dg, dfc = _oracle_dg(inp, dt)
+    _x_case(dg, dfc, inp["w_g"], inp["w_fc"], dt)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 8, 8), (63, 72, 136), (300, 264, 264), (1000, 8, 520),
+                                   (257, 520, 8), (700, 256, 128), (513, 1032, 72),
+                                   (2000, 64, 2048)])
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_gemm_stages_odd_shapes(M, K, N, dt):
+    inp = swiglu_inputs(SwiGLUShape("odd", 13, M, K, N), dtype=dt)
+    dg, dfc = _oracle_dg(inp, dt)
+    _w_case(inp["x"], dg, dfc, dt)
+    _x_case(dg, dfc, inp["w_g"], inp["w_fc"], dt)
+
+
+def test_x_stage_empty_contraction_writes_zero():
+    dev = device()
+    M, K = 33, 16
+    dx = torch.full((M, K), 3.0, dtype=torch.bfloat16, device=dev)
+    e = torch.empty(M, 0, dtype=torch.bfloat16, device=dev)
+    w = torch.empty(K, 0, dtype=torch.bfloat16, device=dev)
+    note("x stage N=0")
+    swg.swiglu_bwd_x(e, e, w, w, dx)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dx).item() == 0
+
+
+def test_chained_b_w_x_on_ragged_batch():
+    """GPU b feeds GPU w and x; compared with the oracle chained in float64."""
+    dev = device()
+    inp = swiglu_inputs("ragged", dtype="bf16")
+    M, N = inp["dy"].shape
+    K = inp["x"].shape[1]
+    d = {k: v.to(dev) for k, v in inp.items()}
+    dg, dfc = torch.empty_like(d["dy"]), torch.empty_like(d["dy"])
+    db_g = torch.zeros(N, dtype=torch.bfloat16, device=dev)
+    db_fc = torch.zeros_like(db_g)
+    dw_g = torch.zeros(K, N, dtype=torch.bfloat16, device=dev)
+    dw_fc = torch.zeros_like(dw_g)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    note("chained b -> w -> x ragged")
+    swg.swiglu_bwd_b(d["dy"], d["g"], d["fc"], dg, dfc, db_g, db_fc)
+    swg.swiglu_bwd_w(d["x"], dg, dfc, dw_g, dw_fc)
+    swg.swiglu_bwd_x(dg, dfc, d["w_g"], d["w_fc"], dx)
+    torch.cuda.synchronize()
+    ref = R.swiglu_bwd_ref(to64(inp["dy"]), to64(inp["x"]), to64(inp["w_g"]), to64(inp["w_fc"]),
+                           to64(inp["g"]), to64(inp["fc"]))
+    got = {"dg": dg, "dfc": dfc, "db_g": db_g, "db_fc": db_fc, "dw_g": dw_g, "dw_fc": dw_fc,
+           "dx": dx}
+    for k, v in got.items():
+        compare(f"chained {k}", v.cpu(), ref[k], "bf16")
+
+
+def test_bitwise_deterministic_reruns():
+    dev = device()
+    inp = swiglu_inputs("ragged", dtype="bf16")
+    d = {k: v.to(dev) for k, v in inp.items()}
+    M, N = inp["dy"].shape
+    K = inp["x"].shape[1]
+    outs = []
+    for _ in range(2):
+        dg, dfc = torch.empty_like(d["dy"]), torch.empty_like(d["dy"])
+        db_g = torch.zeros(N, dtype=torch.bfloat16, device=dev)
+        db_fc = torch.zeros_like(db_g)
+        dw_g = torch.zeros(K, N, dtype=torch.bfloat16, device=dev)
+        dw_fc = torch.zeros_like(dw_g)
+        dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+        swg.swiglu_bwd_b(d["dy"], d["g"], d["fc"], dg, dfc, db_g, db_fc)
+        swg.swiglu_bwd_w(d["x"], dg, dfc, dw_g, dw_fc)
+        swg.swiglu_bwd_x(dg, dfc, d["w_g"], d["w_fc"], dx)
+        torch.cuda.synchronize()
+        outs.append([t.view(torch.int16).cpu() for t in (dg, dfc, db_g, db_fc, dw_g, dw_fc, dx)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
