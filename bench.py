@@ -75,6 +75,7 @@ def cpu_baseline(inp, sw_inputs, rows, swish_len):
     m = min(rows, M)
     dy, g, fc, x = (f64(inp[k][:m]) for k in ("dy", "g", "fc", "x"))
     wg, wf = f64(inp["w_g"]), f64(inp["w_fc"])
+    swish_len = min(swish_len, sw_inputs["fp32"]["grad"].numel())
     sw = {dt: (f64(v["grad"][:swish_len]), f64(v["x"][:swish_len])) for dt, v in sw_inputs.items()}
     t0 = time.perf_counter()
     dg, dfc, _, _ = R.b_ref(dy, g, fc)
@@ -88,9 +89,9 @@ def cpu_baseline(inp, sw_inputs, rows, swish_len):
     return {"value": round(100.0 * t_roof / t, 6), "unit": "% of roofline",
             "cores": int(blas_threads), "kind": "oracle",
             "seconds": round(t, 3),
-            "sample": f"first {m} of {M} rows (b, w, x stages) and first {swish_len} elements "
-                      f"of the Swish input per dtype; numpy float64, element-wise work on 1 "
-                      f"thread, GEMMs on {blas_threads} BLAS threads",
+            "sample": f"{m} of {M} rows (b, w, x stages) and {swish_len} elements of the "
+                      f"Swish input per dtype (whole workload when equal); numpy float64, "
+                      f"element-wise work on 1 thread, GEMMs on {blas_threads} BLAS threads",
             "cpu": _cpu_model()}
 
 
@@ -112,8 +113,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ffn_220k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=49152)
-    ap.add_argument("--cpu-swish-len", type=int, default=1 << 22)
+    ap.add_argument("--cpu-rows", type=int, default=1 << 30,
+                    help="rows of the SwiGLU workload the oracle baseline runs (default: all)")
+    ap.add_argument("--cpu-swish-len", type=int, default=1 << 30,
+                    help="Swish elements per dtype for the oracle baseline (default: all)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

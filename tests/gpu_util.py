@@ -2,7 +2,9 @@
 chunked drive of the float64 oracle over large workloads."""
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -10,6 +12,9 @@ import torch
 
 import oracle.ref as R
 from parity import Checker, dfc_abs_model, dg_abs_model, sum_abs_model, to64
+
+# numpy releases the GIL inside its loops: row blocks of the oracle run on a thread pool
+WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 SENTINEL_BITS = {torch.bfloat16: 0x7FA5, torch.float16: 0x7DA5, torch.float32: 0x7FA5A5A5}
 
@@ -51,37 +56,47 @@ def rne(a64, dtype):
     return torch.from_numpy(np.ascontiguousarray(a64)).to(dtype)
 
 
-def oracle_b_chunked(dy, g, fc, db_g0=None, db_fc0=None, rows=16384, gpu=None, dtype="bf16",
+def oracle_b_chunked(dy, g, fc, db_g0=None, db_fc0=None, rows=4096, gpu=None, dtype="bf16",
                      store_dtype=None):
-    """Run the oracle's b stage over row blocks.
+    """Run the oracle's b stage over row blocks (on a thread pool).
 
-    Returns (db_g, db_fc, sum|dg|, sum|dfc|, dg_rounded, dfc_rounded) where the last two
-    are the oracle's dg/dfc rounded to `store_dtype` (CPU tensors) when requested.  If
-    `gpu` = (dg_gpu, dfc_gpu) CPU tensors is given, they are compared chunk by chunk and
-    the two Checkers are returned as well.
+    Returns a dict with db_g, db_fc (float64, initial values added), abs_g / abs_fc (the
+    column sums of |dg| / |dfc|) and, when `store_dtype` is given, the oracle's dg / dfc
+    rounded to it (CPU tensors).  If `gpu` = (dg_gpu, dfc_gpu) CPU tensors is given they
+    are compared block by block and the two Checkers are returned as check_dg/check_dfc.
     """
     M, N = dy.shape
+    out_g = torch.empty((M, N), dtype=store_dtype) if store_dtype is not None else None
+    out_fc = torch.empty((M, N), dtype=store_dtype) if store_dtype is not None else None
+
+    def block(r0):
+        r1 = min(M, r0 + rows)
+        cdy, cg, cfc = to64(dy[r0:r1]), to64(g[r0:r1]), to64(fc[r0:r1])
+        dgv, dfcv, sg, sf = R.b_ref(cdy, cg, cfc)
+        part = {"sg": sg, "sf": sf, "ag": np.abs(dgv).sum(0), "af": np.abs(dfcv).sum(0)}
+        if out_g is not None:
+            out_g[r0:r1] = rne(dgv, store_dtype)
+            out_fc[r0:r1] = rne(dfcv, store_dtype)
+        if gpu is not None:
+            part["cg"] = Checker("dg", dtype).add(gpu[0][r0:r1], dgv, dg_abs_model(cdy, cg, cfc))
+            part["cf"] = Checker("dfc", dtype).add(gpu[1][r0:r1], dfcv, dfc_abs_model(cdy, cg))
+        return part
+
+    with ThreadPoolExecutor(WORKERS) as ex:
+        parts = list(ex.map(block, range(0, M, rows)))
     db_g = np.zeros(N) if db_g0 is None else to64(db_g0).copy()
     db_fc = np.zeros(N) if db_fc0 is None else to64(db_fc0).copy()
     abs_g, abs_fc = np.zeros(N), np.zeros(N)
-    out_g = torch.empty((M, N), dtype=store_dtype) if store_dtype is not None else None
-    out_fc = torch.empty((M, N), dtype=store_dtype) if store_dtype is not None else None
     ck_g = Checker("dg", dtype) if gpu is not None else None
     ck_fc = Checker("dfc", dtype) if gpu is not None else None
-    for r0 in range(0, M, rows):
-        r1 = min(M, r0 + rows)
-        cdy, cg, cfc = to64(dy[r0:r1]), to64(g[r0:r1]), to64(fc[r0:r1])
-        dg, dfc, sg, sf = R.b_ref(cdy, cg, cfc)
-        db_g += sg
-        db_fc += sf
-        abs_g += np.abs(dg).sum(0)
-        abs_fc += np.abs(dfc).sum(0)
-        if out_g is not None:
-            out_g[r0:r1] = rne(dg, store_dtype)
-            out_fc[r0:r1] = rne(dfc, store_dtype)
+    for p in parts:                 # fixed (row-block) order
+        db_g += p["sg"]
+        db_fc += p["sf"]
+        abs_g += p["ag"]
+        abs_fc += p["af"]
         if gpu is not None:
-            ck_g.add(gpu[0][r0:r1], dg, dg_abs_model(cdy, cg, cfc))
-            ck_fc.add(gpu[1][r0:r1], dfc, dfc_abs_model(cdy, cg))
+            ck_g.merge(p["cg"])
+            ck_fc.merge(p["cf"])
     res = {"db_g": db_g, "db_fc": db_fc, "abs_g": abs_g, "abs_fc": abs_fc,
            "dg": out_g, "dfc": out_fc}
     if gpu is not None:

@@ -123,6 +123,17 @@ class Checker:
                 self.worst = (float(g.flat[i]), float(r.flat[i]))
         return self
 
+    def merge(self, other):
+        """Fold in another Checker's counts (chunks checked on other threads)."""
+        for k in ("n", "nonfinite", "contract_fail", "mixed_fail"):
+            setattr(self, k, getattr(self, k) + getattr(other, k))
+        self.ss_ref += other.ss_ref
+        self.ss_err += other.ss_err
+        self.max_abs_err = max(self.max_abs_err, other.max_abs_err)
+        if other.worst_excess > self.worst_excess:
+            self.worst_excess, self.worst = other.worst_excess, other.worst
+        return self
+
     def result(self, raise_on_fail=True):
         nr, ne = np.sqrt(self.ss_ref), np.sqrt(self.ss_err)
         normwise = ne / nr if nr > 0 else ne
