@@ -6,6 +6,7 @@
 // and the Fused SwiGLU backward page's kernel signatures (section "Kernel 签名与参数规格").
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "../../include/swiglu_bwd.h"
@@ -29,6 +30,30 @@ swg_status hip_status(hipError_t e) {
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Compute units of the current device (cached per device; 0 if the query fails, in
+// which case the launch uses one workgroup per tile).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+int gemm_grid_cap() {
+  const int cus = device_cus();
+  return cus > 0 ? cus : (1 << 30);
+}
 
 }  // namespace
 
@@ -101,6 +126,9 @@ static swg_status gemm_shape_check(int dtype, int64_t M, int64_t K, int64_t N) {
   if (!dtype_ok(dtype) || M < 0 || K < 0 || N < 0) return SWG_ERR_INVALID;
   if (dtype == SWG_FP32) return SWG_ERR_UNSUPPORTED;
   if (K % 8 != 0 || N % 8 != 0) return SWG_ERR_UNSUPPORTED;
+  // tile windows are addressed with 32-bit byte offsets (256 rows of 2N bytes) and
+  // row indices in 32 bits
+  if (K >= kMaxGemmDim || N >= kMaxGemmDim || M >= (int64_t(1) << 31)) return SWG_ERR_UNSUPPORTED;
   return SWG_OK;
 }
 
@@ -123,7 +151,8 @@ swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc, void* dw
   if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
   if (!aligned(workspace, 16)) return SWG_ERR_INVALID;
   return hip_status(launch_w_stage(dtype, p, x, dg, dfc, dw_g, dw_fc, M, K, N,
-                                   static_cast<float*>(workspace), as_stream(stream)));
+                                   static_cast<float*>(workspace), gemm_grid_cap(),
+                                   as_stream(stream)));
 }
 
 swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
@@ -137,7 +166,8 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
     return hip_status(launch_zero(dx, (size_t)M * (size_t)K * 2, as_stream(stream)));
   if (!dg || !dfc || !w_g || !w_fc) return SWG_ERR_NULLPTR;
   for (const void* p : {dg, dfc, w_g, w_fc}) if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
-  return hip_status(launch_x_stage(dtype, dg, dfc, w_g, w_fc, dx, M, K, N, as_stream(stream)));
+  return hip_status(launch_x_stage(dtype, dg, dfc, w_g, w_fc, dx, M, K, N, gemm_grid_cap(),
+                                   as_stream(stream)));
 }
 
 }  // extern "C"

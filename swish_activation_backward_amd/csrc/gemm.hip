@@ -1,28 +1,51 @@
 // Matrix-core kernels for gfx950: the w stage [dw_g | dw_fc] += x^T [dg | dfc]
 // (one TN GEMM [K, M] x [M, 2N]) and the x stage dx = [dg | dfc] [W_g | W_fc]^T
 // (one NT GEMM [M, 2N] x [2N, K]).  Source: the Fused SwiGLU backward page
-// (PyPTO-Gym), formulas 3 and 4, and its matmul transposition flags (w: a
-// transposed, b not; x: a not, b transposed); fp32 accumulation as in its dtype table.
+// (PyPTO-Gym), formulas 3 and 4 and its matmul transposition flags (w: first operand
+// transposed; x: second operand transposed); fp32 accumulation as in its dtype flow.
 //
-// Both kernels compute a 256 x 256 output tile per workgroup from LDS tiles laid out
-// as [rows][contraction] with a 16-byte pad per row, so that every lane fetches its
-// MFMA operand (8 consecutive contraction elements) with one 16-byte LDS read and the
-// 32 rows of a 32 x 32 x 16 MFMA hit distinct banks.  Two LDS stages: while the matrix
-// cores work on stage t, the lanes hold the global loads of stage t + 1 in registers.
+// Both kernels compute a 256 x 256 output tile per workgroup of four wavefronts (one
+// per SIMD); each wave owns a 128 x 128 block = 4 x 4 tiles of v_mfma_f32_32x32x16 whose
+// 256 fp32 accumulators live in the AGPR file.
 //
-//   x stage: both operands are contraction-contiguous in memory, copied as is.
-//   w stage: both operands are contraction-strided (the contraction runs over rows of
-//            x and dg), so each lane loads an 8 x 8 block (8 rows x 16 bytes, fully
-//            coalesced along the row) and transposes it in registers before the LDS
-//            store.
+// Operands move global -> LDS with buffer_load ... lds (the load unit writes LDS
+// directly; no registers, no ds_write).  LDS is a ring of four 32-deep contraction
+// stages (32 KiB each): while the matrix cores work on stage t, stages t+1..t+3 are in
+// flight, and a stage is consumed only after `s_waitcnt vmcnt` says this wave's part of
+// it landed and a barrier says every wave's part did.  Rows and columns outside the
+// tensors (ragged M, partial tiles, stages past the end) are fetched at offsets beyond
+// the buffer window and arrive as zeros from the hardware range check: the loop has no
+// data-path branches.
 //
-// Workgroup ids are remapped so that consecutive logical tiles run on one XCD
-// (the hardware deals consecutive ids round-robin over the 8 XCDs): tiles that share
-// an operand panel then share that XCD's L2.
+//   x stage: both operands are contraction-contiguous in memory; LDS keeps them as
+//            [row][32 contraction] and each lane reads one MFMA operand (8 consecutive
+//            contraction elements) with a 16-byte ds_read_b128.
+//   w stage: both operands are contraction-strided (the contraction runs over the rows
+//            of x and dg); LDS keeps them as loaded, [32 contraction][256 columns], and
+//            the operands are read with the gfx950 transposing LDS read
+//            ds_read_b64_tr_b16 (two per operand).
+// Every LDS tile is XOR-swizzled in 16-byte chunks (the swizzle is applied to the
+// global address each lane fetches, since the LDS write order is fixed by the load
+// unit) so that the operand reads of one instruction hit distinct banks.
+//
+// The concatenations [dg | dfc] and [W_g | W_fc] are never materialised: the x stage
+// runs its contraction over dg/W_g and then dfc/W_fc, and the w stage gives each
+// output tile one of dg or dfc.
+//
+// Both kernels are persistent: one workgroup per CU walks a list of output tiles and the
+// ring keeps streaming across tile boundaries (the first stages of the next tile are in
+// flight while the current tile finishes and writes its result straight from the
+// accumulators).  Work is dealt so that concurrently running tiles with neighbouring
+// indices sit on one XCD (the hardware deals workgroup ids round-robin over the 8
+// XCDs): tiles sharing an operand panel then share that XCD's L2.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace swg {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+#define LDS_AS __attribute__((address_space(3)))
 
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16> {
@@ -38,11 +61,44 @@ template <> struct Mfma<fp16> {
   }
 };
 
-constexpr int BP = kTileP, BQ = kTileQ, BR = kTileR;
-constexpr int LDR = BR + 8;            // LDS row stride (elements): 144 bytes
-constexpr int STAGE = (BP + BQ) * LDR;  // elements per LDS stage
-constexpr int LDC = BQ + 8;            // LDS row stride of the staged output tile
-static_assert(BP * LDC <= 2 * STAGE, "output staging must fit in the operand stages");
+constexpr int BP = kTileP, BQ = kTileQ, BR = kTileR;   // 256 x 256 tile, 32-deep stages
+constexpr int NT = 256;                                 // 4 wavefronts, 2 x 2
+constexpr int WP = 2, WQ = 2;
+constexpr int FP = BP / WP / 32, FQ = BQ / WQ / 32;     // 4 x 4 MFMA tiles per wave
+constexpr int SLOT = (BP + BQ) * BR;                    // elements per ring slot (32 KiB)
+constexpr int LOADS_PER_STAGE = SLOT * 2 / 1024 / (NT / 64);   // 1 KiB loads per wave: 8
+constexpr uint32_t kOOB = 0x80000000u;  // offset past every window: loads zeros
+static_assert(BR == 32 && BP == 256 && BQ == 256, "swizzles below assume 256 x 256 x 32");
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+constexpr int vmcnt_le(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
+constexpr int kLgkmcnt0 = 0xC07F;   // s_waitcnt lgkmcnt(0), other counters free
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer, no stride: offsets >= bytes return zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ inline uint32_t clamp_bytes(int64_t rows, int64_t row_bytes) {
+  return rows > 0 ? (uint32_t)(rows * row_bytes) : 0u;
+}
+// 16 bytes per lane from `off` in window `r` to LDS at dst + OFS + 16 * lane (dst must be
+// wave-uniform).  Issued as inline asm: the loads' completion is tracked by the explicit
+// vmcnt waits of the pipeline (the compiler's own tracking of LDS-DMA stores would add
+// conservative waits that drain the ring).  The constant OFS is added to M0 inside the
+// asm so one scalar base serves all loads of a stage.
+template <int OFS>
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint16_t* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(LDS_AS const void*)dst);
+  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(r), "s"(lds), "i"(OFS)
+               : "memory", "scc");   // s_add_u32 writes SCC
+}
+// Compiler-only fence: keeps LDS reads and writes on their side of a barrier without
+// emitting the memory-model waits of __syncthreads (which would drain the ring).
+#define SWG_COMPILER_FENCE() asm volatile("" ::: "memory")
 
 // consecutive logical tiles -> same XCD
 __device__ inline int64_t xcd_remap(int64_t b, int64_t nblocks) {
@@ -51,251 +107,438 @@ __device__ inline int64_t xcd_remap(int64_t b, int64_t nblocks) {
   return (b % 8) * per + b / 8;
 }
 
-// ----------------------------------------------------------------- compute core
-// WP x WQ wavefronts; each owns a (BP / WP) x (BQ / WQ) block of 32 x 32 MFMA tiles.
-// MFMA 32x32x16 operand layout: lane l supplies row (l % 32), contraction elements
-// 8 (l / 32) .. 8 (l / 32) + 7; the accumulator lane l holds column (l % 32) and rows
-// 8 (r / 4) + 4 (l / 32) + (r % 4) for r = 0..15.
-template <int WP_, int WQ_>
-struct Waves {
-  static constexpr int WP = WP_, WQ = WQ_;
-  static constexpr int NT = 64 * WP * WQ;
-  static constexpr int FP = BP / WP / 32, FQ = BQ / WQ / 32;
-};
-// 8 wavefronts (2 per SIMD), each 128 x 64: 128 accumulator registers per lane.
-typedef Waves<2, 4> GemmWaves;
-
-template <typename T, class C>
-__device__ inline void mma_stage(const uint16_t* As, const uint16_t* Bs, int wp, int wq, int lane,
-                                 f32x16 (&acc)[C::FP][C::FQ]) {
-  constexpr int WP = C::WP, WQ = C::WQ, FP = C::FP, FQ = C::FQ;
-  using F = typename Mfma<T>::frag;
-  const int lrow = lane & 31;
-  const int lk = (lane >> 5) * 8;
-#pragma unroll
-  for (int kk = 0; kk < BR; kk += 16) {
-    F a[FP], b[FQ];
-#pragma unroll
-    for (int i = 0; i < FP; ++i)
-      a[i] = *reinterpret_cast<const F*>(As + (wp * (BP / WP) + i * 32 + lrow) * LDR + kk + lk);
-#pragma unroll
-    for (int j = 0; j < FQ; ++j)
-      b[j] = *reinterpret_cast<const F*>(Bs + (wq * (BQ / WQ) + j * 32 + lrow) * LDR + kk + lk);
-#pragma unroll
-    for (int i = 0; i < FP; ++i)
-#pragma unroll
-      for (int j = 0; j < FQ; ++j) acc[i][j] = Mfma<T>::mma(a[i], b[j], acc[i][j]);
-  }
-}
-
-// ----------------------------------------------------------------- x stage (NT)
-// A = [dg | dfc] rows p (M), B = [W_g | W_fc] rows q (K); contraction over 2N.
-template <typename T, class C>
-__global__ __launch_bounds__(C::NT) void x_stage_kernel(
-    const T* __restrict__ dg, const T* __restrict__ dfc, const T* __restrict__ wg,
-    const T* __restrict__ wfc, T* __restrict__ dx, int64_t M, int64_t K, int64_t N,
-    int64_t nq) {
-  constexpr int WP = C::WP, WQ = C::WQ, FP = C::FP, FQ = C::FQ, NT = C::NT;
-  constexpr int XCH = (BP * BR / 8) / NT;  // 16-byte chunks per lane per operand
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wp = wave / WQ, wq = wave % WQ;
-  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t p0 = (L / nq) * BP, q0 = (L % nq) * BQ;
-  const int64_t R = 2 * N;
-  const int64_t nsteps = (R + BR - 1) / BR;
-
-  f32x16 acc[FP][FQ];
+__device__ inline void zero_acc(f32x16 (&acc)[FP][FQ]) {
 #pragma unroll
   for (int i = 0; i < FP; ++i)
 #pragma unroll
     for (int j = 0; j < FQ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
 
-  u32x4 ra[XCH], rb[XCH];
-  auto load = [&](int64_t r0) {
-#pragma unroll
-    for (int c = 0; c < XCH; ++c) {
-      const int id = tid + c * NT;
-      const int row = id >> 3, ch = id & 7;
-      const int64_t rr = r0 + ch * 8;
-      const int64_t p = p0 + row, q = q0 + row;
-      u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-      if (rr < R) {
-        const bool lo = rr < N;
-        const int64_t col = lo ? rr : rr - N;
-        if (p < M) va = ld16((lo ? dg : dfc) + p * N + col);
-        if (q < K) vb = ld16((lo ? wg : wfc) + q * N + col);
-      }
-      ra[c] = va;
-      rb[c] = vb;
-    }
-  };
-  auto store = [&](int buf) {
-    uint16_t* As = lds + buf * STAGE;
-    uint16_t* Bs = As + BP * LDR;
-#pragma unroll
-    for (int c = 0; c < XCH; ++c) {
-      const int id = tid + c * NT;
-      const int row = id >> 3, ch = id & 7;
-      st16(As + row * LDR + ch * 8, ra[c]);
-      st16(Bs + row * LDR + ch * 8, rb[c]);
-    }
-  };
+// MFMA 32x32x16 layout: lane l supplies row (l % 32) and contraction elements
+// 8 (l / 32) .. 8 (l / 32) + 7 of each operand; accumulator register r of lane l holds
+// row 8 (r / 4) + 4 (l / 32) + (r % 4), column l % 32.
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int64_t t = 0; t < nsteps; ++t) {
-    const int buf = (int)(t & 1);
-    if (t + 1 < nsteps) load((t + 1) * BR);
-    mma_stage<T, C>(lds + buf * STAGE, lds + buf * STAGE + BP * LDR, wp, wq, lane, acc);
-    if (t + 1 < nsteps) store(buf ^ 1);
-    __syncthreads();
+// ------------------------------------------------------------------ x-stage tiles
+// Slot layout: [256 rows of A][32] then [256 rows of B][32]; a row is 4 chunks of 16 B.
+// Chunk c of row r sits at position c ^ xsw(r): for any 8 consecutive rows, and any 16,
+// the 16-byte reads of one MFMA operand land on distinct banks.
+__device__ inline int xsw(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Scheduling hints: sched_group_barrier(mask, n, 0) asks the scheduler for n
+// instructions of the class next (0x008 MFMA, 0x100 LDS read).  Pattern per stage:
+// the 8 operand reads of the first 16-deep step, then the 8 reads of the second step
+// spread between the first step's MFMAs, then the second step's MFMAs.
+#define SWG_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+template <int FIRST_READS, int READS_PER_PAIR>
+__device__ inline void stage_schedule() {
+  SWG_SCHED(0x100, FIRST_READS);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    SWG_SCHED(0x008, 2);
+    SWG_SCHED(0x100, READS_PER_PAIR);
   }
+  SWG_SCHED(0x008, 16);
+}
 
-  // epilogue: round to T, stage the 256 x 256 tile in LDS, write 16-byte rows
-  T* Cs = reinterpret_cast<T*>(lds);
+template <typename T>
+__device__ inline void x_compute(const uint16_t* slot, int wp, int wq, int lane,
+                                 f32x16 (&acc)[FP][FQ]) {
+  using F = typename Mfma<T>::frag;
+  F a[2][FP], b[2][FQ];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int lc = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FP; ++i) {
+      const int r = wp * 128 + i * 32 + (lane & 31);
+      a[kk][i] = *reinterpret_cast<const F*>(slot + r * BR + ((lc ^ xsw(r)) << 3));
+    }
+#pragma unroll
+    for (int j = 0; j < FQ; ++j) {
+      const int r = wq * 128 + j * 32 + (lane & 31);
+      b[kk][j] = *reinterpret_cast<const F*>(slot + (BP + r) * BR + ((lc ^ xsw(r)) << 3));
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+#pragma unroll
+      for (int j = 0; j < FQ; ++j) acc[i][j] = Mfma<T>::mma(a[kk][i], b[kk][j], acc[i][j]);
+  stage_schedule<8, 1>();
+}
+
+// ------------------------------------------------------------------ w-stage tiles
+// Slot layout: [32 contraction rows of A][256] then [32 rows of B][256]; a row is 32
+// chunks of 16 B, chunk c of row m at position c ^ wsw(m).  A transposing read covers
+// 4 rows x 32 bytes per 16 lanes (64 bytes for 32 lanes); wsw spreads them over
+// distinct banks.
+__device__ inline int wsw(int m) {
+  const int t = m & 3;
+  return t == 0 ? 0 : t == 1 ? 6 : t == 2 ? 12 : 10;
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane s supplies 4 consecutive 16-bit
+// elements E[s][0..3]; lane i receives E[4 j + i / 4][i % 4] for j = 0..3.  With lane s
+// pointing at row m0 + s / 4, column c0 + 4 (s % 4), lane i gets column c0 + i of rows
+// m0 .. m0 + 3: four consecutive contraction elements of one operand row.
+__device__ inline i16x4 tr_read(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p);
+}
+
+// Per-lane part of the transposing-read address of operand block i (rows 32 i .. of the
+// wave's 128), in elements, for contraction rows 0..3 of a 16-row step:
+//   lane = 16 grp + s:  row 8 (grp / 2) + s / 4, column 32 i + 16 (grp % 2) + 4 (s % 4)
+// with the column's chunk swizzled by wsw(row) (row % 4 = s / 4: the swizzle does not
+// depend on the step or on i's contribution above bit 3, so every other term is a
+// compile-time offset).
+__device__ inline void w_lane_offsets(int lane, int (&off)[FP]) {
+  const int grp = lane >> 4, s = lane & 15;
+  const int q = 2 * (grp & 1) + ((s & 3) >> 1);    // chunk inside the 32-column block
+  const int sw = wsw(s >> 2);
+  const int row = 8 * (grp >> 1) + (s >> 2);
+#pragma unroll
+  for (int i = 0; i < FP; ++i) off[i] = row * BQ + (((4 * i + q) ^ sw) << 3) + 4 * (s & 1);
+}
+
+template <typename T>
+__device__ inline typename Mfma<T>::frag w_frag(const uint16_t* p) {
+  // p: this lane's address for contraction rows 0..3; rows 4..7 are 4 rows further
+  const i16x4 lo = tr_read(p);
+  const i16x4 hi = tr_read(p + 4 * BQ);
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(typename Mfma<T>::frag, v);
+}
+
+template <typename T>
+__device__ inline void w_compute(const uint16_t* slot, const int (&aoff)[FP],
+                                 const int (&boff)[FQ], f32x16 (&acc)[FP][FQ]) {
+  using F = typename Mfma<T>::frag;
+  F a[2][FP], b[2][FQ];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int i = 0; i < FP; ++i) a[ks][i] = w_frag<T>(slot + 16 * ks * BQ + aoff[i]);
+#pragma unroll
+    for (int j = 0; j < FQ; ++j)
+      b[ks][j] = w_frag<T>(slot + BR * BP + 16 * ks * BQ + boff[j]);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+#pragma unroll
+      for (int j = 0; j < FQ; ++j) acc[i][j] = Mfma<T>::mma(a[ks][i], b[ks][j], acc[i][j]);
+  stage_schedule<16, 2>();   // two transposing reads per operand
+}
+
+// One pipeline step: the stage in slot `cur` is consumed while the stage three ahead is
+// issued into `nxt` (the slot consumed one step earlier).  Every issue is
+// LOADS_PER_STAGE loads per wave, always issued (stages past the end of the work load
+// zeros), so "the stage in cur has landed" is exactly "at most 2 stages of loads
+// outstanding".  The barrier also tells every wave that all reads of `nxt` are done.
+#define SWG_RING_STEP(ISSUE_NEXT, COMPUTE, cur, nxt)            \
+  do {                                                          \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));  \
+    SWG_COMPILER_FENCE();                                       \
+    __builtin_amdgcn_s_barrier();                               \
+    SWG_COMPILER_FENCE();                                       \
+    ISSUE_NEXT(nxt);                                            \
+    COMPUTE(cur);                                               \
+  } while (0)
+
+// Swap a value with the neighbouring lane (lane ^ 1): DPP quad_perm [1, 0, 3, 2].
+__device__ inline float swap_adjacent(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// Two adjacent columns of one row, rounded to T (nearest even) and packed in 32 bits.
+template <typename T> __device__ inline uint32_t pack2(float lo, float hi);
+template <> __device__ inline uint32_t pack2<bf16>(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+template <> __device__ inline uint32_t pack2<fp16>(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+template <typename T> __device__ inline float2 unpack2(uint32_t v);
+template <> __device__ inline float2 unpack2<bf16>(uint32_t v) {
+  return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+}
+template <> __device__ inline float2 unpack2<fp16>(uint32_t v) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 h = __builtin_bit_cast(f16x2, v);
+  return make_float2((float)h[0], (float)h[1]);
+}
+
+// Visit the accumulators of a wave as row pairs of adjacent columns: accumulator
+// registers r and r + 1 of a 32 x 32 tile are rows R and R + 1 of one column; after a
+// swap with the neighbouring lane, even lanes hold (row R, columns c, c + 1) and odd
+// lanes (row R + 1, columns c - 1, c).  fn(row, col, lo, hi) gets tile-local
+// coordinates (row, col even).
+template <typename Fn>
+__device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane, Fn&& fn) {
+  const int odd = lane & 1;
 #pragma unroll
   for (int i = 0; i < FP; ++i)
 #pragma unroll
     for (int j = 0; j < FQ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wp * (BP / WP) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = wq * (BQ / WQ) + j * 32 + (lane & 31);
-        Cs[row * LDC + col] = from_f32<T>(acc[i][j][r]);
+      for (int r = 0; r < 16; r += 2) {
+        const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+        const float recv = swap_adjacent(odd ? v0 : v1);
+        const float lo = odd ? recv : v0, hi = odd ? v1 : recv;
+        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + odd;
+        const int col = j * 32 + ((lane & 31) & ~1);
+        fn(row, col, lo, hi);
       }
-  __syncthreads();
-  constexpr int CCH = BP * BQ / 8 / NT;
-#pragma unroll 4
-  for (int c = 0; c < CCH; ++c) {
-    const int id = tid + c * NT;
-    const int row = id / (BQ / 8), ch = id % (BQ / 8);
-    const int64_t p = p0 + row, q = q0 + ch * 8;
-    if (p < M && q < K)
-      st16(dx + p * K + q, *reinterpret_cast<const u32x4*>(Cs + row * LDC + ch * 8));
+}
+
+// One tile's run of the ring: nst stages (a multiple of 4).  The issue side runs three
+// stages ahead, so the last three issues of a tile fetch the first stages of the next
+// tile (`nxt`); keeping that hand-over in a peeled last round leaves the steady-state
+// rounds free of branches, so the scheduler can overlap the MFMAs of one step with the
+// barrier and loads of the next.
+#define SWG_TILE_ROUNDS(ISSUE, COMPUTE, cur_ctx, nxt_ctx, nst)                                \
+  do {                                                                                    \
+    int64_t t_ = 0;                                                                       \
+    for (; t_ + 4 < (nst); t_ += 4) {                                                     \
+      SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 3, sl); }, COMPUTE, ring,      \
+                    ring + 3 * SLOT);                                                     \
+      SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 4, sl); }, COMPUTE,            \
+                    ring + SLOT, ring);                                                   \
+      SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 5, sl); }, COMPUTE,            \
+                    ring + 2 * SLOT, ring + SLOT);                                        \
+      SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 6, sl); }, COMPUTE,            \
+                    ring + 3 * SLOT, ring + 2 * SLOT);                                    \
+    }                                                                                     \
+    SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 3, sl); }, COMPUTE, ring,        \
+                  ring + 3 * SLOT);                                                       \
+    SWG_RING_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 0, sl); }, COMPUTE, ring + SLOT, ring); \
+    SWG_RING_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 1, sl); }, COMPUTE, ring + 2 * SLOT,  \
+                  ring + SLOT);                                                           \
+    SWG_RING_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 2, sl); }, COMPUTE, ring + 3 * SLOT,  \
+                  ring + 2 * SLOT);                                                       \
+  } while (0)
+
+// ----------------------------------------------------------------- x stage (NT)
+// A = [dg | dfc] rows p (M), B = [W_g | W_fc] rows q (K).  Stage s < sN contracts over
+// columns 32 s .. of dg / W_g, stage s >= sN over the same columns of dfc / W_fc (sN is
+// rounded up to even so that a tile is a whole number of 4-stage ring rounds; the extra
+// stages read zeros).  Tile L covers rows (L / nq) * 256 and columns (L % nq) * 256.
+struct XTile {   // first row of the dg/dfc panel and of the W panel; 32-bit (M < 2^31)
+  int p0, q0;
+  bool live;
+};
+
+__device__ inline XTile x_tile(int64_t L, bool live, int64_t nq) {
+  XTile c;
+  c.live = live;
+  const int64_t LL = live ? L : 0;
+  c.p0 = (int)(LL / nq) * BP;
+  c.q0 = (int)(LL % nq) * BQ;
+  return c;
+}
+
+template <typename T>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void x_stage_kernel(
+    const T* __restrict__ dg, const T* __restrict__ dfc, const T* __restrict__ wg,
+    const T* __restrict__ wfc, T* __restrict__ dx, int64_t M, int64_t K, int64_t N, int64_t nq,
+    int64_t ntiles) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[4 * SLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wp = wave / WQ, wq = wave % WQ;
+  const int64_t G = gridDim.x;
+  const int64_t f0 = xcd_remap(blockIdx.x, G);
+  const int64_t my_tiles = ntiles > f0 ? (ntiles - f0 + G - 1) / G : 0;
+  const int64_t sN = 2 * ((N + 2 * BR - 1) / (2 * BR));
+  const int64_t nst = 2 * sN;
+
+  // A 1 KiB load covers 16 rows x 4 chunks; this wave's loads are rows
+  // 64 wave + 16 i + lane / 4 (i = 0..3) of A and of B.  The lane fetches logical chunk
+  // (lane % 4) ^ xsw(row), so LDS position lane % 4 of the row holds it swizzled.
+  uint32_t roff[4];
+  int lcol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 64 * wave + 16 * i + (lane >> 2);
+    roff[i] = (uint32_t)row * (uint32_t)(N * 2);
+    lcol[i] = ((lane & 3) ^ xsw(row)) * 8;
   }
+  auto issue = [&](const XTile& c, int64_t s, uint16_t* slot) {
+    const bool hi = s >= sN;
+    const int64_t col0 = (hi ? s - sN : s) * BR;
+    const int rows_a = c.live ? ((int)M - c.p0 < BP ? (int)M - c.p0 : BP) : 0;
+    const int rows_b = c.live ? ((int)K - c.q0 < BQ ? (int)K - c.q0 : BQ) : 0;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc((hi ? dfc : dg) + (int64_t)c.p0 * N, clamp_bytes(rows_a, N * 2));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc((hi ? wfc : wg) + (int64_t)c.q0 * N, clamp_bytes(rows_b, N * 2));
+    const uint16_t* dst = slot + 64 * wave * BR;   // this wave's 4 rows-of-16 blocks
+    uint32_t off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t col = col0 + lcol[i];
+      off[i] = col < N ? roff[i] + (uint32_t)(col * 2) : kOOB;
+    }
+    dma16<0 * 16 * BR * 2>(ra, off[0], dst);
+    dma16<1 * 16 * BR * 2>(ra, off[1], dst);
+    dma16<2 * 16 * BR * 2>(ra, off[2], dst);
+    dma16<3 * 16 * BR * 2>(ra, off[3], dst);
+    dma16<BP * BR * 2 + 0 * 16 * BR * 2>(rb, off[0], dst);
+    dma16<BP * BR * 2 + 1 * 16 * BR * 2>(rb, off[1], dst);
+    dma16<BP * BR * 2 + 2 * 16 * BR * 2>(rb, off[2], dst);
+    dma16<BP * BR * 2 + 3 * 16 * BR * 2>(rb, off[3], dst);
+  };
+#define X_ISSUE(c, s, slot) issue((c), (s), (slot))
+#define X_COMPUTE(slot) x_compute<T>((slot), wp, wq, lane, acc)
+
+  f32x16 acc[FP][FQ];
+  XTile cur = x_tile(f0, my_tiles > 0, nq);
+  issue(cur, 0, ring);
+  issue(cur, 1, ring + SLOT);
+  issue(cur, 2, ring + 2 * SLOT);
+  for (int64_t j = 0; j < my_tiles; ++j) {
+    const XTile nxt = x_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
+    zero_acc(acc);
+    SWG_TILE_ROUNDS(X_ISSUE, X_COMPUTE, cur, nxt, nst);
+    // epilogue: straight from the accumulators, two adjacent columns per 32-bit store
+    const int64_t p0 = (int64_t)cur.p0 + wp * 128, q0 = (int64_t)cur.q0 + wq * 128;
+    for_each_pair(acc, lane, [&](int row, int col, float lo, float hi) {
+      const int64_t p = p0 + row, q = q0 + col;
+      if (p < M && q < K) *reinterpret_cast<uint32_t*>(dx + p * K + q) = pack2<T>(lo, hi);
+    });
+    cur = nxt;
+  }
+#undef X_ISSUE
+#undef X_COMPUTE
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
 // ----------------------------------------------------------------- w stage (TN)
-// A = x^T: rows k (K), contraction m;  B = [dg | dfc]^T: rows n (2N), contraction m.
-// 8 x 8 blocks of 16-bit elements: 256 per operand per stage.
-static_assert(BP == BQ, "w-stage block split assumes square tiles");
+// A = x^T: rows k (K), contraction m;  B = d^T (d = dg or dfc): rows n, contraction m.
+// Work item L = (split s, tile tt): rows [s R, min(M, (s + 1) R)) of the contraction,
+// output rows k0 = (tt / (2 tnh)) * 256, columns n0 of dg (tt % (2 tnh) < tnh) or of dfc.
+struct WItem {   // 32-bit fields: M < 2^31 and K, N < 2^22 are checked on the host
+  int s, k0, n0, m_begin, m_end, nst;
+  bool hi, live;
+};
 
-__device__ inline void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-  // in[i]: 8 halves of source row i; out[j]: the 8 rows' half j
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int d = j >> 1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t a = in[2 * e][d], b = in[2 * e + 1][d];
-      out[j][e] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
+__device__ inline WItem w_item(int64_t L, bool live, int64_t tiles, int64_t tnh,
+                               int64_t split_rows, int64_t M) {
+  WItem w;
+  w.live = live;
+  const int64_t LL = live ? L : 0;
+  w.s = (int)(LL / tiles);
+  const int tt = (int)(LL % tiles);
+  const int kb = tt / (int)(2 * tnh), nb = tt % (int)(2 * tnh);
+  w.hi = nb >= tnh;
+  w.k0 = kb * BP;
+  w.n0 = (w.hi ? nb - (int)tnh : nb) * BQ;
+  w.m_begin = w.s * (int)split_rows;
+  w.m_end = (w.m_begin + split_rows < M) ? w.m_begin + (int)split_rows : (int)M;
+  w.nst = 4 * ((w.m_end - w.m_begin + 4 * BR - 1) / (4 * BR));   // whole ring rounds
+  return w;
 }
 
-template <typename T, class C>
-__global__ __launch_bounds__(C::NT) void w_stage_kernel(
+template <typename T>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void w_stage_kernel(
     const T* __restrict__ x, const T* __restrict__ dg, const T* __restrict__ dfc,
     T* __restrict__ dwg, T* __restrict__ dwfc, float* __restrict__ ws, int64_t M, int64_t K,
-    int64_t N, int64_t tn, int64_t tiles, int64_t split_rows) {
-  constexpr int WP = C::WP, WQ = C::WQ, FP = C::FP, FQ = C::FQ, NT = C::NT;
-  constexpr int WBLK = (2 * (BP * BR / 64)) / NT;  // 8 x 8 blocks per lane per stage
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int64_t N, int64_t tnh, int64_t tiles, int64_t split_rows, int64_t nitems) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[4 * SLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / WQ, wq = wave % WQ;
-  const int64_t L = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t s = L / tiles, tt = L % tiles;
-  const int64_t k0 = (tt / tn) * BP, n0 = (tt % tn) * BQ;
-  const int64_t m_begin = s * split_rows;
-  const int64_t m_end = (m_begin + split_rows < M) ? m_begin + split_rows : M;
-  const int64_t R2 = 2 * N;
-  const int64_t nsteps = (m_end - m_begin + BR - 1) / BR;
+  const int64_t G = gridDim.x;
+  const int64_t f0 = xcd_remap(blockIdx.x, G);
+  const int64_t my_items = nitems > f0 ? (nitems - f0 + G - 1) / G : 0;
+
+  // A 1 KiB load covers 2 rows x 32 chunks; this wave's loads are rows 8 wave + 2 i +
+  // lane / 32 (i = 0..3) of A and of B, logical chunk (lane % 32) ^ wsw(row).  The lane
+  // parts of the offsets are fixed; the tile adds k0 / n0 (uniform).
+  uint32_t xbase[4], dbase[4];
+  int lcol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * wave + 2 * i + (lane >> 5);
+    lcol[i] = ((lane & 31) ^ wsw(row)) * 8;
+    xbase[i] = (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)lcol[i] * 2u;
+    dbase[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)lcol[i] * 2u;
+  }
+  // one buffer window per stage: rows m0 .. m0 + 32 (rows past m_end, and every row of
+  // a dead item, read 0)
+  auto issue = [&](const WItem& w, int64_t st, uint16_t* slot) {
+    const int m0 = w.m_begin + (int)st * BR;
+    const int rows = w.live ? ((w.m_end - m0 < BR) ? w.m_end - m0 : BR) : 0;
+    const int64_t mb = rows > 0 ? m0 : 0;
+    const T* d = w.hi ? dfc : dg;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + mb * K, clamp_bytes(rows, K * 2));
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(d + mb * N, clamp_bytes(rows, N * 2));
+    const int kleft = (int)K - w.k0, nleft = (int)N - w.n0;   // columns left in the tile
+    const uint32_t k2 = (uint32_t)w.k0 * 2u, n2 = (uint32_t)w.n0 * 2u;
+    const uint16_t* dst = slot + 8 * wave * BP;   // this wave's 4 row pairs
+    dma16<0 * 2 * BP * 2>(rx, lcol[0] < kleft ? xbase[0] + k2 : kOOB, dst);
+    dma16<1 * 2 * BP * 2>(rx, lcol[1] < kleft ? xbase[1] + k2 : kOOB, dst);
+    dma16<2 * 2 * BP * 2>(rx, lcol[2] < kleft ? xbase[2] + k2 : kOOB, dst);
+    dma16<3 * 2 * BP * 2>(rx, lcol[3] < kleft ? xbase[3] + k2 : kOOB, dst);
+    dma16<BR * BP * 2 + 0 * 2 * BP * 2>(rd, lcol[0] < nleft ? dbase[0] + n2 : kOOB, dst);
+    dma16<BR * BP * 2 + 1 * 2 * BP * 2>(rd, lcol[1] < nleft ? dbase[1] + n2 : kOOB, dst);
+    dma16<BR * BP * 2 + 2 * 2 * BP * 2>(rd, lcol[2] < nleft ? dbase[2] + n2 : kOOB, dst);
+    dma16<BR * BP * 2 + 3 * 2 * BP * 2>(rd, lcol[3] < nleft ? dbase[3] + n2 : kOOB, dst);
+  };
+
+  int aoff[FP], boff[FQ];
+  w_lane_offsets(lane, aoff);
+#pragma unroll
+  for (int i = 0; i < FP; ++i) {
+    boff[i] = aoff[i] + wq * 128;
+    aoff[i] += wp * 128;
+  }
+#define W_ISSUE(c, s, slot) issue((c), (s), (slot))
+#define W_COMPUTE(slot) w_compute<T>((slot), aoff, boff, acc)
 
   f32x16 acc[FP][FQ];
-#pragma unroll
-  for (int i = 0; i < FP; ++i)
-#pragma unroll
-    for (int j = 0; j < FQ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  u32x4 rin[WBLK][8];
-  auto load = [&](int64_t m0) {
-#pragma unroll
-    for (int bI = 0; bI < WBLK; ++bI) {
-      const int id = tid + bI * NT;
-      const bool isA = id < (BP * BR / 64);
-      const int bid = isA ? id : id - (BP * BR / 64);
-      const int bc = bid & 31, bm = bid >> 5;  // 8-column group, 8-row group
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t m = m0 + bm * 8 + i;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (m < m_end) {
-          if (isA) {
-            const int64_t k = k0 + bc * 8;
-            if (k < K) v = ld16(x + m * K + k);
-          } else {
-            const int64_t n = n0 + bc * 8;
-            if (n < R2) v = ld16(n < N ? dg + m * N + n : dfc + m * N + (n - N));
-          }
+  WItem cur = w_item(f0, my_items > 0, tiles, tnh, split_rows, M);
+  issue(cur, 0, ring);
+  issue(cur, 1, ring + SLOT);
+  issue(cur, 2, ring + 2 * SLOT);
+  const int64_t R2 = 2 * N;
+  for (int64_t j = 0; j < my_items; ++j) {
+    const WItem nxt = w_item(f0 + (j + 1) * G, j + 1 < my_items, tiles, tnh, split_rows, M);
+    zero_acc(acc);
+    SWG_TILE_ROUNDS(W_ISSUE, W_COMPUTE, cur, nxt, cur.nst);
+    // epilogue: rows k, columns n (of dg or dfc) straight from the accumulators
+    const int64_t k0 = (int64_t)cur.k0 + wp * 128, n0 = (int64_t)cur.n0 + wq * 128;
+    if (ws != nullptr) {
+      // fp32 partials in the [K, 2N] layout of split s
+      float* dst = ws + (int64_t)cur.s * K * R2 + (cur.hi ? N : 0);
+      for_each_pair(acc, lane, [&](int row, int col, float lo, float hi) {
+        const int64_t k = k0 + row, n = n0 + col;
+        if (k < K && n < N) *reinterpret_cast<float2*>(dst + k * R2 + n) = make_float2(lo, hi);
+      });
+    } else {
+      T* dw = cur.hi ? dwfc : dwg;
+      for_each_pair(acc, lane, [&](int row, int col, float lo, float hi) {
+        const int64_t k = k0 + row, n = n0 + col;
+        if (k < K && n < N) {
+          uint32_t* p = reinterpret_cast<uint32_t*>(dw + k * N + n);
+          const float2 old = unpack2<T>(*p);
+          *p = pack2<T>(old.x + lo, old.y + hi);
         }
-        rin[bI][i] = v;
-      }
+      });
     }
-  };
-  auto store = [&](int buf) {
-    uint16_t* As = lds + buf * STAGE;
-    uint16_t* Bs = As + BP * LDR;
-#pragma unroll
-    for (int bI = 0; bI < WBLK; ++bI) {
-      const int id = tid + bI * NT;
-      const bool isA = id < (BP * BR / 64);
-      const int bid = isA ? id : id - (BP * BR / 64);
-      const int bc = bid & 31, bm = bid >> 5;
-      u32x4 out[8];
-      transpose8x8(rin[bI], out);
-      uint16_t* base = (isA ? As : Bs) + (bc * 8) * LDR + bm * 8;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) st16(base + j * LDR, out[j]);
-    }
-  };
-
-  if (nsteps > 0) {
-    load(m_begin);
-    store(0);
+    cur = nxt;
   }
-  __syncthreads();
-  for (int64_t t = 0; t < nsteps; ++t) {
-    const int buf = (int)(t & 1);
-    if (t + 1 < nsteps) load(m_begin + (t + 1) * BR);
-    mma_stage<T, C>(lds + buf * STAGE, lds + buf * STAGE + BP * LDR, wp, wq, lane, acc);
-    if (t + 1 < nsteps) store(buf ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: rows k, cols n of the [K, 2N] result
-#pragma unroll
-  for (int i = 0; i < FP; ++i)
-#pragma unroll
-    for (int j = 0; j < FQ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t k = k0 + wp * (BP / WP) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t n = n0 + wq * (BQ / WQ) + j * 32 + (lane & 31);
-        if (k < K && n < R2) {
-          if (ws != nullptr) {
-            ws[(s * K + k) * R2 + n] = acc[i][j][r];
-          } else {
-            T* dst = n < N ? dwg + k * N + n : dwfc + k * N + (n - N);
-            *dst = from_f32<T>(to_f32(*dst) + acc[i][j][r]);
-          }
-        }
-      }
+#undef W_ISSUE
+#undef W_COMPUTE
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
 // dw = RNE(dw + sum_s ws[s]) in split order; 4 consecutive columns per lane (N % 8 == 0,
@@ -319,7 +562,6 @@ __global__ __launch_bounds__(256) void w_reduce_kernel(const float* __restrict__
   }
 }
 
-template <typename T>
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, int64_t words) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words;
        i += (int64_t)gridDim.x * 256)
@@ -328,32 +570,36 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, int64_t wor
 
 template <typename T>
 static hipError_t x_stage_t(const void* dg, const void* dfc, const void* wg, const void* wfc,
-                            void* dx, int64_t M, int64_t K, int64_t N, hipStream_t stream) {
+                            void* dx, int64_t M, int64_t K, int64_t N, int cus,
+                            hipStream_t stream) {
   const int64_t np = ceil_div(M, BP), nq = ceil_div(K, BQ);
-  hipLaunchKernelGGL((x_stage_kernel<T, GemmWaves>), dim3((unsigned)(np * nq)),
-                     dim3(GemmWaves::NT), 0,
-                     stream, static_cast<const T*>(dg), static_cast<const T*>(dfc),
+  const int64_t ntiles = np * nq;
+  const int64_t grid = ntiles < cus ? ntiles : cus;
+  hipLaunchKernelGGL((x_stage_kernel<T>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                     static_cast<const T*>(dg), static_cast<const T*>(dfc),
                      static_cast<const T*>(wg), static_cast<const T*>(wfc), static_cast<T*>(dx),
-                     M, K, N, nq);
+                     M, K, N, nq, ntiles);
   return hipGetLastError();
 }
 
 hipError_t launch_x_stage(int dtype, const void* dg, const void* dfc, const void* w_g,
-                          const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N,
+                          const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
                           hipStream_t stream) {
-  if (dtype == 0) return x_stage_t<bf16>(dg, dfc, w_g, w_fc, dx, M, K, N, stream);
-  return x_stage_t<fp16>(dg, dfc, w_g, w_fc, dx, M, K, N, stream);
+  if (dtype == 0) return x_stage_t<bf16>(dg, dfc, w_g, w_fc, dx, M, K, N, cus, stream);
+  return x_stage_t<fp16>(dg, dfc, w_g, w_fc, dx, M, K, N, cus, stream);
 }
 
 template <typename T>
 static hipError_t w_stage_t(const WPlan& p, const void* x, const void* dg, const void* dfc,
                             void* dwg, void* dwfc, int64_t M, int64_t K, int64_t N, float* ws,
-                            hipStream_t stream) {
+                            int cus, hipStream_t stream) {
   float* wsp = p.splits > 1 ? ws : nullptr;
-  hipLaunchKernelGGL((w_stage_kernel<T, GemmWaves>), dim3((unsigned)(p.splits * p.tiles)),
-                     dim3(GemmWaves::NT), 0, stream, static_cast<const T*>(x),
-                     static_cast<const T*>(dg), static_cast<const T*>(dfc), static_cast<T*>(dwg),
-                     static_cast<T*>(dwfc), wsp, M, K, N, p.tn, p.tiles, p.rows);
+  const int64_t nitems = p.splits * p.tiles;
+  const int64_t grid = nitems < cus ? nitems : cus;
+  hipLaunchKernelGGL((w_stage_kernel<T>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                     static_cast<const T*>(x), static_cast<const T*>(dg),
+                     static_cast<const T*>(dfc), static_cast<T*>(dwg), static_cast<T*>(dwfc), wsp,
+                     M, K, N, p.tn / 2, p.tiles, p.rows, nitems);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   int64_t blocks = ceil_div(K * 2 * N / 4, 256);
@@ -365,9 +611,9 @@ static hipError_t w_stage_t(const WPlan& p, const void* x, const void* dg, const
 
 hipError_t launch_w_stage(int dtype, const WPlan& p, const void* x, const void* dg,
                           const void* dfc, void* dw_g, void* dw_fc, int64_t M, int64_t K,
-                          int64_t N, float* ws, hipStream_t stream) {
-  if (dtype == 0) return w_stage_t<bf16>(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, stream);
-  return w_stage_t<fp16>(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, stream);
+                          int64_t N, float* ws, int cus, hipStream_t stream) {
+  if (dtype == 0) return w_stage_t<bf16>(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, cus, stream);
+  return w_stage_t<fp16>(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, cus, stream);
 }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
@@ -375,7 +621,7 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
   int64_t blocks = ceil_div(words, 256);
   if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL((fill_zero_kernel<int>), dim3((unsigned)blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<uint32_t*>(p), words);
   return hipGetLastError();
 }

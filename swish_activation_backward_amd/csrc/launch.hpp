@@ -17,12 +17,14 @@ hipError_t launch_b_stage(int dtype, const BPlan& p, const void* dy, const void*
                           const void* fc, void* dg, void* dfc, void* db_g, void* db_fc,
                           int64_t M, int64_t N, float* part, hipStream_t stream);
 
+// `cus`: compute units of the device: the GEMM stages launch one persistent workgroup
+// per CU (fewer when there is less work).
 hipError_t launch_w_stage(int dtype, const WPlan& p, const void* x, const void* dg,
                           const void* dfc, void* dw_g, void* dw_fc, int64_t M, int64_t K,
-                          int64_t N, float* ws, hipStream_t stream);
+                          int64_t N, float* ws, int cus, hipStream_t stream);
 
 hipError_t launch_x_stage(int dtype, const void* dg, const void* dfc, const void* w_g,
-                          const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N,
+                          const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
                           hipStream_t stream);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);

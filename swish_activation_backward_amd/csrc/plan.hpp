@@ -61,12 +61,13 @@ inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
 // Both GEMMs use 256 x 256 output tiles and a 64-deep contraction step per LDS stage.
 constexpr int kTileP = 256;     // output rows per workgroup
 constexpr int kTileQ = 256;     // output cols per workgroup
-constexpr int kTileR = 64;      // contraction depth per LDS stage
+constexpr int kTileR = 32;      // contraction depth per LDS stage
+constexpr int64_t kMaxGemmDim = int64_t(1) << 22;  // K, N limit of the GEMM stages
 
 // w stage: output [K, 2N]; when it has too few tiles to fill the chip the batch
 // dimension M is split into S ranges whose fp32 partials are summed in order.
 struct WPlan {
-  int64_t tk, tn, tiles;   // tile grid over [K, 2N]
+  int64_t tk, tn, tiles;   // tile grid over [K, 2N]: tn / 2 column tiles in dg, tn / 2 in dfc
   int64_t splits;          // S
   int64_t rows;            // rows of M per split (multiple of kTileR)
   size_t ws_bytes;         // S > 1: S * K * 2N * sizeof(float)
@@ -78,7 +79,7 @@ constexpr int64_t kWMinRowsPerSplit = 512;
 inline WPlan plan_w(int64_t M, int64_t K, int64_t N) {
   WPlan p{};
   p.tk = ceil_div(K, kTileP);
-  p.tn = ceil_div(2 * N, kTileQ);
+  p.tn = 2 * ceil_div(N, kTileQ);
   p.tiles = p.tk * p.tn;
   int64_t s = p.tiles > 0 ? ceil_div(kWTargetBlocks, p.tiles) : 1;
   const int64_t smax = M / kWMinRowsPerSplit;
