@@ -10,6 +10,8 @@
 // Both streaming kernels read each input once with 16-byte non-temporal loads
 // (8 bf16/fp16 or 4 fp32 per lane, so one wave instruction moves 1 KiB), keep several
 // independent loads in flight per lane, and write each output once.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -100,44 +102,48 @@ hipError_t launch_swish_grad(int dtype, const void* grad, const void* x, void* o
 // ------------------------------------------------------------------ b stage
 // Workgroup = 256 lanes laid out as TY rows x TX vector-columns (TX = 2^txlog2).
 // blockIdx.x picks the column strip, blockIdx.y the row chunk.  Each lane walks the
-// chunk's rows with stride TY (two rows per step for more loads in flight), writes
-// dg and dfc, and keeps fp32 column sums; the workgroup reduces them over TY in
-// LDS (fixed order) and writes one partial row: part[chunk][0:N] = sum dg,
-// part[chunk][N:2N] = sum dfc.
+// chunk's rows with stride TY; on the vector path it first issues the loads of R rows
+// (3R independent 16-byte loads in flight per lane), then computes and stores them.
+// dg and dfc are written with non-temporal stores: the next stage reads them back
+// from HBM anyway (they are far larger than the caches).  The lane keeps fp32 column
+// sums; the workgroup reduces them over TY in LDS (fixed order) and writes one
+// partial row: part[chunk][0:N] = sum dg, part[chunk][N:2N] = sum dfc.
 template <typename T, bool VECTOR>
 struct BAccess {
   static constexpr int V = VECTOR ? Vec16<T>::VEC : 1;
-  __device__ static inline void load(const T* p, float* f) {
-    if constexpr (VECTOR) {
-      Vec16<T>::widen(ld16_stream(p), f);
-    } else {
-      f[0] = to_f32(*p);
-    }
+  using Raw = typename std::conditional<VECTOR, u32x4, T>::type;
+  __device__ static inline Raw load(const T* p) {
+    if constexpr (VECTOR) return ld16_stream(p);
+    else return *p;
+  }
+  __device__ static inline void widen(const Raw& r, float* f) {
+    if constexpr (VECTOR) Vec16<T>::widen(r, f);
+    else f[0] = to_f32(r);
   }
   __device__ static inline void store(T* p, const float* f) {
-    if constexpr (VECTOR) {
-      st16(p, Vec16<T>::narrow(f));
-    } else {
-      *p = from_f32<T>(f[0]);
-    }
+    if constexpr (VECTOR) st16_stream(p, Vec16<T>::narrow(f));
+    else *p = from_f32<T>(f[0]);
   }
 };
 
+// dg = dy fc s (1 + g (1 - s)),  dfc = dy g s  (SwiGLU page, formulas 1 and 2)
 template <typename T, bool VECTOR>
-__device__ inline void b_row(const T* dy, const T* g, const T* fc, T* dg, T* dfc, int64_t off,
-                             float* sg, float* sf) {
+__device__ inline void b_compute(const typename BAccess<T, VECTOR>::Raw& rdy,
+                                 const typename BAccess<T, VECTOR>::Raw& rg,
+                                 const typename BAccess<T, VECTOR>::Raw& rfc, T* dg, T* dfc,
+                                 int64_t off, float* sg, float* sf) {
   using A = BAccess<T, VECTOR>;
   constexpr int V = A::V;
   float fdy[V], fg[V], ffc[V], odg[V], odfc[V];
-  A::load(dy + off, fdy);
-  A::load(g + off, fg);
-  A::load(fc + off, ffc);
+  A::widen(rdy, fdy);
+  A::widen(rg, fg);
+  A::widen(rfc, ffc);
 #pragma unroll
   for (int e = 0; e < V; ++e) {
     const SigmoidParts p = sigmoid_parts(fg[e]);
     const float dyfc = fdy[e] * ffc[e];
-    odg[e] = dyfc * __builtin_fmaf(fg[e], p.s1ms, p.s);   // dy fc s (1 + g (1 - s))
-    odfc[e] = fdy[e] * (fg[e] * p.s);                      // dy g s
+    odg[e] = dyfc * __builtin_fmaf(fg[e], p.s1ms, p.s);
+    odfc[e] = fdy[e] * (fg[e] * p.s);
     sg[e] += odg[e];
     sf[e] += odfc[e];
   }
@@ -145,11 +151,12 @@ __device__ inline void b_row(const T* dy, const T* g, const T* fc, T* dg, T* dfc
   A::store(dfc + off, odfc);
 }
 
-template <typename T, bool VECTOR>
+template <typename T, bool VECTOR, int R>
 __global__ __launch_bounds__(256) void b_stage_kernel(const T* dy, const T* g, const T* fc, T* dg,
                                                       T* dfc, float* part, int64_t M, int64_t N,
                                                       int64_t cv, int64_t rows, int txlog2) {
-  constexpr int V = BAccess<T, VECTOR>::V;
+  using A = BAccess<T, VECTOR>;
+  constexpr int V = A::V;
   const int tid = threadIdx.x;
   const int TX = 1 << txlog2;
   const int TY = 256 >> txlog2;
@@ -166,11 +173,24 @@ __global__ __launch_bounds__(256) void b_stage_kernel(const T* dy, const T* g, c
   if (c < cv) {
     const int64_t col = c * V;
     int64_t r = r0 + ty;
-    for (; r + TY < r1; r += 2 * TY) {
-      b_row<T, VECTOR>(dy, g, fc, dg, dfc, r * N + col, sg, sf);
-      b_row<T, VECTOR>(dy, g, fc, dg, dfc, (r + TY) * N + col, sg, sf);
+    for (; r + (R - 1) * TY < r1; r += R * TY) {
+      typename A::Raw a[R], b[R], d[R];
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int64_t off = (r + u * TY) * N + col;
+        a[u] = A::load(dy + off);
+        b[u] = A::load(g + off);
+        d[u] = A::load(fc + off);
+      }
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+        b_compute<T, VECTOR>(a[u], b[u], d[u], dg, dfc, (r + u * TY) * N + col, sg, sf);
     }
-    if (r < r1) b_row<T, VECTOR>(dy, g, fc, dg, dfc, r * N + col, sg, sf);
+    for (; r < r1; r += TY) {
+      const int64_t off = r * N + col;
+      b_compute<T, VECTOR>(A::load(dy + off), A::load(g + off), A::load(fc + off), dg, dfc, off,
+                           sg, sf);
+    }
   }
 
   __shared__ float red[2 * 8 * 256];
@@ -192,9 +212,13 @@ __global__ __launch_bounds__(256) void b_stage_kernel(const T* dy, const T* g, c
   }
 }
 
-// db[n] = RNE(db[n] + sum_chunks part[chunk][n]): 16 columns x 16 chunk groups per
-// workgroup; group j sums chunks j, j+16, ... in order, then the 16 group sums are
-// added in order (fixed summation tree: deterministic, depth nchunks/16 + 16).
+// db[n] = RNE(db[n] + sum_chunks part[chunk][n]).  A workgroup owns 16 columns of the
+// [nchunks, 2N] partial matrix; its 16 lane groups split the chunks round-robin
+// (group j takes chunks j, j+16, ...), each lane keeping kFinUnroll loads in flight
+// and adding them in chunk order; the 16 group sums are then added in group order.
+// The summation tree depends only on nchunks: results are run-to-run deterministic.
+constexpr int kFinUnroll = 16;
+
 template <typename T>
 __global__ __launch_bounds__(256) void db_finalize_kernel(const float* part, T* db_g, T* db_fc,
                                                           int64_t N, int64_t nchunks) {
@@ -203,8 +227,18 @@ __global__ __launch_bounds__(256) void db_finalize_kernel(const float* part, T* 
   const int64_t col = (int64_t)blockIdx.x * 16 + lane;
   const int64_t W = 2 * N;
   float s = 0.0f;
-  if (col < W)
-    for (int64_t ch = grp; ch < nchunks; ch += 16) s += part[ch * W + col];
+  if (col < W) {
+    for (int64_t ch0 = grp; ch0 < nchunks; ch0 += 16 * kFinUnroll) {
+      float v[kFinUnroll];
+#pragma unroll
+      for (int u = 0; u < kFinUnroll; ++u) {
+        const int64_t ch = ch0 + 16 * u;
+        v[u] = ch < nchunks ? part[ch * W + col] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kFinUnroll; ++u) s += v[u];
+    }
+  }
   __shared__ float red[16][17];
   red[grp][lane] = s;
   __syncthreads();
@@ -228,11 +262,11 @@ static hipError_t b_stage_t(const BPlan& p, const void* dy, const void* g, const
   const T* b = static_cast<const T*>(g);
   const T* c = static_cast<const T*>(fc);
   if (p.vec > 1) {
-    hipLaunchKernelGGL((b_stage_kernel<T, true>), grid, dim3(256), 0, stream, a, b, c,
+    hipLaunchKernelGGL((b_stage_kernel<T, true, kBRowsInFlight>), grid, dim3(256), 0, stream, a, b, c,
                        static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.rows,
                        txlog2);
   } else {
-    hipLaunchKernelGGL((b_stage_kernel<T, false>), grid, dim3(256), 0, stream, a, b, c,
+    hipLaunchKernelGGL((b_stage_kernel<T, false, 1>), grid, dim3(256), 0, stream, a, b, c,
                        static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.rows,
                        txlog2);
   }

@@ -30,6 +30,7 @@ struct BPlan {
 constexpr int kBThreads = 256;
 constexpr int64_t kBTargetBlocks = 2048;
 constexpr int64_t kBMinRows = 32;
+constexpr int kBRowsInFlight = 4;   // rows whose loads a lane issues before computing
 
 inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
   BPlan p{};
