@@ -33,6 +33,14 @@ SWISH_BETA = 1.702
 SWISH_DTYPES = ("fp32", "fp16", "bf16")
 ES = {"fp32": 4, "fp16": 2, "bf16": 2}
 
+# Kernel sources, hashed to tell whether recorded HBM counters still describe the code.
+KERNEL_SOURCES = {
+    "b_stage_kernel": "swish_activation_backward_amd/csrc/elementwise.hip",
+    "w_stage_kernel": "swish_activation_backward_amd/csrc/gemm.hip",
+    "x_stage_kernel": "swish_activation_backward_amd/csrc/gemm.hip",
+    "swish_grad_vec_kernel": "swish_activation_backward_amd/csrc/elementwise.hip",
+}
+
 KERNELS = {
     "b": ["b_stage_kernel", "db_finalize_kernel"],
     "w": ["w_stage_kernel", "w_reduce_kernel"],
@@ -56,6 +64,42 @@ def stage_work(M, K, N, L):
         v["bound"] = "mfma" if t_mma > t_mem else "hbm"
         v["t_roof"] = max(t_mem, t_mma)
     return w
+
+
+def source_sha256(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+    of this workload (scaled by the plain-copy calibration recorded with it), or None when
+    there is no summary or the kernel's source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    try:
+        with open(path) as f:
+            text = f.read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(block)["kernels"][kernel]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    src = KERNEL_SOURCES.get(kernel)
+    if src is None or rec.get("source_sha256") != source_sha256(src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes, reps=5):
+    """A plain device-to-device copy of `nbytes`, for scaling the HBM byte counters."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": reps}), flush=True)
 
 
 def cpu_baseline(inp, sw_inputs, rows, swish_len):
@@ -113,8 +157,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ffn_220k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES bytes (counter calibration) and exit")
     ap.add_argument("--cpu-rows", type=int, default=1 << 30,
-                    help="rows of the SwiGLU workload the oracle baseline runs (default: all)")
+                    help="rows of the SwiGLU workload the oracle baseline runs (default: all "
+                         "of them; a few seconds of float64 work on a 16-core host)")
     ap.add_argument("--cpu-swish-len", type=int, default=1 << 30,
                     help="Swish elements per dtype for the oracle baseline (default: all)")
     args = ap.parse_args()
@@ -127,6 +174,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
 
     import swish_activation_backward_amd as swg
     from workloads.gen import SWIGLU_WORKLOADS, SWISH_WORKLOAD, swiglu_inputs, swish_inputs
@@ -217,7 +268,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(wk["bytes"] / t / 1e9, 1),
                 "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(args.workload, stages[dom]["kernels"][0])
     roof["stage"] = dom
     roof["kernels"] = stages[dom]["kernels"]
     roof["avg_launch_us"] = stages[dom]["us"]
