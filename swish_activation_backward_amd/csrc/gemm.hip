@@ -10,9 +10,10 @@
 //
 // Operands move global -> LDS with buffer_load ... lds (the load unit writes LDS
 // directly; no registers, no ds_write).  LDS is a ring of four 32-deep contraction
-// stages (32 KiB each): while the matrix cores work on stage t, stages t+1..t+3 are in
-// flight, and a stage is consumed only after `s_waitcnt vmcnt` says this wave's part of
-// it landed and a barrier says every wave's part did.  Rows and columns outside the
+// stages (32 KiB each), and operand fragments are double-buffered in registers: while the
+// matrix cores multiply stage t from registers, the fragments of stage t+1 are read from
+// LDS and stages t+2..t+4 are in flight.  A stage is read only after `s_waitcnt vmcnt`
+// says this wave's part of it landed and a barrier says every wave's part did.  Rows and columns outside the
 // tensors (ragged M, partial tiles, stages past the end) are fetched at offsets beyond
 // the buffer window and arrive as zeros from the hardware range check: the loop has no
 // data-path branches.
@@ -126,50 +127,44 @@ __device__ inline void zero_acc(f32x16 (&acc)[FP][FQ]) {
 // the 16-byte reads of one MFMA operand land on distinct banks.
 __device__ inline int xsw(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// Scheduling hints: sched_group_barrier(mask, n, 0) asks the scheduler for n
-// instructions of the class next (0x008 MFMA, 0x100 LDS read).  Pattern per stage:
-// the 8 operand reads of the first 16-deep step, then the 8 reads of the second step
-// spread between the first step's MFMAs, then the second step's MFMAs.
+// Scheduling hint for one pipeline step: the LDS reads of the next stage (READS of them)
+// spread evenly between the 32 MFMAs of the current stage.  sched_group_barrier(mask, n,
+// 0) asks the scheduler for n instructions of the class next (0x008 MFMA, 0x100 LDS read).
 #define SWG_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-template <int FIRST_READS, int READS_PER_PAIR>
-__device__ inline void stage_schedule() {
-  SWG_SCHED(0x100, FIRST_READS);
+template <int READS>
+__device__ inline void step_schedule() {
+  constexpr int kMfmaPerRead = 32 / READS;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    SWG_SCHED(0x008, 2);
-    SWG_SCHED(0x100, READS_PER_PAIR);
+  for (int q = 0; q < READS; ++q) {
+    SWG_SCHED(0x008, kMfmaPerRead);
+    SWG_SCHED(0x100, 1);
   }
-  SWG_SCHED(0x008, 16);
 }
 
+// Operand fragments of one stage, per wave: [contraction half][block]; FragSet[2] holds
+// the stage being multiplied and the stage being read.
+template <typename T> struct FragSet {
+  typename Mfma<T>::frag a[2][FP], b[2][FQ];
+};
+
 template <typename T>
-__device__ inline void x_compute(const uint16_t* slot, int wp, int wq, int lane,
-                                 f32x16 (&acc)[FP][FQ]) {
+__device__ inline void x_read(const uint16_t* slot, int wp, int wq, int lane, FragSet<T>& f) {
   using F = typename Mfma<T>::frag;
-  F a[2][FP], b[2][FQ];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int lc = 2 * kk + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < FP; ++i) {
       const int r = wp * 128 + i * 32 + (lane & 31);
-      a[kk][i] = *reinterpret_cast<const F*>(slot + r * BR + ((lc ^ xsw(r)) << 3));
+      f.a[kk][i] = *reinterpret_cast<const F*>(slot + r * BR + ((lc ^ xsw(r)) << 3));
     }
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
       const int r = wq * 128 + j * 32 + (lane & 31);
-      b[kk][j] = *reinterpret_cast<const F*>(slot + (BP + r) * BR + ((lc ^ xsw(r)) << 3));
+      f.b[kk][j] = *reinterpret_cast<const F*>(slot + (BP + r) * BR + ((lc ^ xsw(r)) << 3));
     }
   }
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int i = 0; i < FP; ++i)
-#pragma unroll
-      for (int j = 0; j < FQ; ++j) acc[i][j] = Mfma<T>::mma(a[kk][i], b[kk][j], acc[i][j]);
-  stage_schedule<8, 1>();
 }
-
 // ------------------------------------------------------------------ w-stage tiles
 // Slot layout: [32 contraction rows of A][256] then [32 rows of B][256]; a row is 32
 // chunks of 16 B, chunk c of row m at position c ^ wsw(m).  A transposing read covers
@@ -213,40 +208,48 @@ __device__ inline typename Mfma<T>::frag w_frag(const uint16_t* p) {
 }
 
 template <typename T>
-__device__ inline void w_compute(const uint16_t* slot, const int (&aoff)[FP],
-                                 const int (&boff)[FQ], f32x16 (&acc)[FP][FQ]) {
-  using F = typename Mfma<T>::frag;
-  F a[2][FP], b[2][FQ];
+__device__ inline void w_read(const uint16_t* slot, const int (&aoff)[FP], const int (&boff)[FQ],
+                              FragSet<T>& f) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int i = 0; i < FP; ++i) a[ks][i] = w_frag<T>(slot + 16 * ks * BQ + aoff[i]);
+    for (int i = 0; i < FP; ++i) f.a[ks][i] = w_frag<T>(slot + 16 * ks * BQ + aoff[i]);
 #pragma unroll
-    for (int j = 0; j < FQ; ++j)
-      b[ks][j] = w_frag<T>(slot + BR * BP + 16 * ks * BQ + boff[j]);
+    for (int j = 0; j < FQ; ++j) f.b[ks][j] = w_frag<T>(slot + BR * BP + 16 * ks * BQ + boff[j]);
   }
+}
+
+// The 32 MFMAs of one stage.
+template <typename T>
+__device__ inline void stage_mma(const FragSet<T>& f, f32x16 (&acc)[FP][FQ]) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int i = 0; i < FP; ++i)
 #pragma unroll
-      for (int j = 0; j < FQ; ++j) acc[i][j] = Mfma<T>::mma(a[ks][i], b[ks][j], acc[i][j]);
-  stage_schedule<16, 2>();   // two transposing reads per operand
+      for (int j = 0; j < FQ; ++j) acc[i][j] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j], acc[i][j]);
 }
 
-// One pipeline step: the stage in slot `cur` is consumed while the stage three ahead is
-// issued into `nxt` (the slot consumed one step earlier).  Every issue is
-// LOADS_PER_STAGE loads per wave, always issued (stages past the end of the work load
-// zeros), so "the stage in cur has landed" is exactly "at most 2 stages of loads
-// outstanding".  The barrier also tells every wave that all reads of `nxt` are done.
-#define SWG_RING_STEP(ISSUE_NEXT, COMPUTE, cur, nxt)            \
-  do {                                                          \
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));  \
-    SWG_COMPILER_FENCE();                                       \
-    __builtin_amdgcn_s_barrier();                               \
-    SWG_COMPILER_FENCE();                                       \
-    ISSUE_NEXT(nxt);                                            \
-    COMPUTE(cur);                                               \
+// One pipeline step u (0..3) of a ring round.  On entry the fragments of the stage in
+// slot u are in registers (set u % 2) and the three following stages are in flight.  The
+// step waits until this wave's loads of the stage in slot u + 1 have landed and its own
+// LDS reads are complete; the barrier then says that every wave's loads landed and that
+// every wave has finished reading slot u, which is refilled with the stage four ahead.
+// The MFMAs of the current stage run from registers while the next stage's fragments
+// are read from LDS into the other set.  Every issue is LOADS_PER_STAGE loads per wave,
+// always issued (stages past the end of the work load zeros), so "the stage in slot u + 1
+// has landed" is exactly "at most 2 stages of loads outstanding".
+#define SWG_PIPE_STEP(ISSUE_AHEAD, READ, frags, u)                        \
+  do {                                                                    \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));            \
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                \
+    SWG_COMPILER_FENCE();                                                 \
+    __builtin_amdgcn_s_barrier();                                         \
+    SWG_COMPILER_FENCE();                                                 \
+    ISSUE_AHEAD(ring + (u) * SLOT);                                       \
+    READ(ring + (((u) + 1) & 3) * SLOT, frags[((u) + 1) & 1]);            \
+    stage_mma<T>(frags[(u) & 1], acc);                                    \
+    step_schedule<READS_PER_STEP>();                                      \
   } while (0)
 
 // Swap a value with the neighbouring lane (lane ^ 1): DPP quad_perm [1, 0, 3, 2].
@@ -299,31 +302,39 @@ __device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane, Fn&&
       }
 }
 
-// One tile's run of the ring: nst stages (a multiple of 4).  The issue side runs three
-// stages ahead, so the last three issues of a tile fetch the first stages of the next
-// tile (`nxt`); keeping that hand-over in a peeled last round leaves the steady-state
-// rounds free of branches, so the scheduler can overlap the MFMAs of one step with the
-// barrier and loads of the next.
-#define SWG_TILE_ROUNDS(ISSUE, COMPUTE, cur_ctx, nxt_ctx, nst)                                \
-  do {                                                                                    \
-    int64_t t_ = 0;                                                                       \
-    for (; t_ + 4 < (nst); t_ += 4) {                                                     \
-      SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 3, sl); }, COMPUTE, ring,      \
-                    ring + 3 * SLOT);                                                     \
-      SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 4, sl); }, COMPUTE,            \
-                    ring + SLOT, ring);                                                   \
-      SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 5, sl); }, COMPUTE,            \
-                    ring + 2 * SLOT, ring + SLOT);                                        \
-      SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 6, sl); }, COMPUTE,            \
-                    ring + 3 * SLOT, ring + 2 * SLOT);                                    \
-    }                                                                                     \
-    SWG_RING_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 3, sl); }, COMPUTE, ring,        \
-                  ring + 3 * SLOT);                                                       \
-    SWG_RING_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 0, sl); }, COMPUTE, ring + SLOT, ring); \
-    SWG_RING_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 1, sl); }, COMPUTE, ring + 2 * SLOT,  \
-                  ring + SLOT);                                                           \
-    SWG_RING_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 2, sl); }, COMPUTE, ring + 3 * SLOT,  \
-                  ring + 2 * SLOT);                                                       \
+// One tile's run of the ring: nst stages (a multiple of 4).  The issue side runs four
+// stages ahead and the LDS reads one stage ahead, so the last four issues of a tile fetch
+// the first stages of the next tile (`nxt_ctx`) and its last step reads the next tile's
+// first stage; keeping that hand-over in a peeled last round leaves the steady-state
+// rounds free of branches.
+#define SWG_TILE_ROUNDS(ISSUE, READ, frags, cur_ctx, nxt_ctx, nst)                             \
+  do {                                                                                     \
+    int64_t t_ = 0;                                                                        \
+    for (; t_ + 4 < (nst); t_ += 4) {                                                      \
+      SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 4, sl); }, READ, frags, 0);     \
+      SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 5, sl); }, READ, frags, 1);     \
+      SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 6, sl); }, READ, frags, 2);     \
+      SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 7, sl); }, READ, frags, 3);     \
+    }                                                                                      \
+    SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 0, sl); }, READ, frags, 0);            \
+    SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 1, sl); }, READ, frags, 1);            \
+    SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 2, sl); }, READ, frags, 2);            \
+    SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 3, sl); }, READ, frags, 3);            \
+  } while (0)
+
+// Pipeline start: the first four stages of the first tile in flight, the first stage's
+// fragments in registers (set 0).
+#define SWG_PIPE_PROLOGUE(ISSUE, READ, frags, ctx)                 \
+  do {                                                             \
+    ISSUE(ctx, 0, ring);                                           \
+    ISSUE(ctx, 1, ring + SLOT);                                    \
+    ISSUE(ctx, 2, ring + 2 * SLOT);                                \
+    ISSUE(ctx, 3, ring + 3 * SLOT);                                \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * LOADS_PER_STAGE));     \
+    SWG_COMPILER_FENCE();                                          \
+    __builtin_amdgcn_s_barrier();                                  \
+    SWG_COMPILER_FENCE();                                          \
+    READ(ring, frags[0]);                                          \
   } while (0)
 
 // ----------------------------------------------------------------- x stage (NT)
@@ -397,17 +408,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     dma16<BP * BR * 2 + 3 * 16 * BR * 2>(rb, off[3], dst);
   };
 #define X_ISSUE(c, s, slot) issue((c), (s), (slot))
-#define X_COMPUTE(slot) x_compute<T>((slot), wp, wq, lane, acc)
+#define X_READ(slot, f) x_read<T>((slot), wp, wq, lane, (f))
+  constexpr int READS_PER_STEP = 16;   // ds_read_b128: 8 per operand
 
   f32x16 acc[FP][FQ];
+  FragSet<T> frags[2];
   XTile cur = x_tile(f0, my_tiles > 0, nq);
-  issue(cur, 0, ring);
-  issue(cur, 1, ring + SLOT);
-  issue(cur, 2, ring + 2 * SLOT);
+  SWG_PIPE_PROLOGUE(X_ISSUE, X_READ, frags, cur);
   for (int64_t j = 0; j < my_tiles; ++j) {
     const XTile nxt = x_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
     zero_acc(acc);
-    SWG_TILE_ROUNDS(X_ISSUE, X_COMPUTE, cur, nxt, nst);
+    SWG_TILE_ROUNDS(X_ISSUE, X_READ, frags, cur, nxt, nst);
     // epilogue: straight from the accumulators, two adjacent columns per 32-bit store
     const int64_t p0 = (int64_t)cur.p0 + wp * 128, q0 = (int64_t)cur.q0 + wq * 128;
     for_each_pair(acc, lane, [&](int row, int col, float lo, float hi) {
@@ -417,7 +428,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     cur = nxt;
   }
 #undef X_ISSUE
-#undef X_COMPUTE
+#undef X_READ
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
@@ -502,18 +513,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     aoff[i] += wp * 128;
   }
 #define W_ISSUE(c, s, slot) issue((c), (s), (slot))
-#define W_COMPUTE(slot) w_compute<T>((slot), aoff, boff, acc)
+#define W_READ(slot, f) w_read<T>((slot), aoff, boff, (f))
+  constexpr int READS_PER_STEP = 32;   // ds_read_b64_tr_b16: 2 per fragment
 
   f32x16 acc[FP][FQ];
+  FragSet<T> frags[2];
   WItem cur = w_item(f0, my_items > 0, tiles, tnh, split_rows, M);
-  issue(cur, 0, ring);
-  issue(cur, 1, ring + SLOT);
-  issue(cur, 2, ring + 2 * SLOT);
+  SWG_PIPE_PROLOGUE(W_ISSUE, W_READ, frags, cur);
   const int64_t R2 = 2 * N;
   for (int64_t j = 0; j < my_items; ++j) {
     const WItem nxt = w_item(f0 + (j + 1) * G, j + 1 < my_items, tiles, tnh, split_rows, M);
     zero_acc(acc);
-    SWG_TILE_ROUNDS(W_ISSUE, W_COMPUTE, cur, nxt, cur.nst);
+    SWG_TILE_ROUNDS(W_ISSUE, W_READ, frags, cur, nxt, cur.nst);
     // epilogue: rows k, columns n (of dg or dfc) straight from the accumulators
     const int64_t k0 = (int64_t)cur.k0 + wp * 128, n0 = (int64_t)cur.n0 + wq * 128;
     if (ws != nullptr) {
@@ -537,7 +548,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     cur = nxt;
   }
 #undef W_ISSUE
-#undef W_COMPUTE
+#undef W_READ
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
