@@ -73,11 +73,14 @@ static hipError_t swish_grad_t(const void* grad, const void* x, void* out, int64
   const T* xx = static_cast<const T*>(x);
   T* o = static_cast<T*>(out);
   if (vector_path) {
-    constexpr int U = 4;
+    // two 16-byte vectors of each input per lane in flight, at most 4096 workgroups
+    // (grid-stride beyond that)
+    constexpr int U = 2;
+    constexpr int64_t kMaxBlocks = 4096;
     constexpr int V = Vec16<T>::VEC;
     const int64_t nvec = n / V;
     int64_t blocks = ceil_div(nvec, 256 * U);
-    if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
+    if (blocks > kMaxBlocks) blocks = kMaxBlocks;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL((swish_grad_vec_kernel<T, U>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, g, xx, o, n, beta);
@@ -101,13 +104,14 @@ hipError_t launch_swish_grad(int dtype, const void* grad, const void* x, void* o
 
 // ------------------------------------------------------------------ b stage
 // Workgroup = 256 lanes laid out as TY rows x TX vector-columns (TX = 2^txlog2).
-// blockIdx.x picks the column strip, blockIdx.y the row chunk.  Each lane walks the
-// chunk's rows with stride TY; on the vector path it first issues the loads of R rows
-// (3R independent 16-byte loads in flight per lane), then computes and stores them.
-// dg and dfc are written with non-temporal stores: the next stage reads them back
-// from HBM anyway (they are far larger than the caches).  The lane keeps fp32 column
-// sums; the workgroup reduces them over TY in LDS (fixed order) and writes one
-// partial row: part[chunk][0:N] = sum dg, part[chunk][N:2N] = sum dfc.
+// blockIdx.x picks the column strip; blockIdx.y is the walker, which takes the row units
+// blockIdx.y, blockIdx.y + gridDim.y, ... (kBUnitRows rows each).  Inside a unit each
+// lane walks the rows with stride TY; on the vector path it first issues the loads of R
+// rows (3R independent 16-byte loads in flight per lane), then computes and stores them.
+// dg and dfc are written with non-temporal stores: the next stage reads them back from
+// HBM anyway (they are far larger than the caches).  The lane keeps fp32 column sums
+// over all its units; the workgroup reduces them over TY in LDS (fixed order) and writes
+// one partial row: part[walker][0:N] = sum dg, part[walker][N:2N] = sum dfc.
 template <typename T, bool VECTOR>
 struct BAccess {
   static constexpr int V = VECTOR ? Vec16<T>::VEC : 1;
@@ -154,7 +158,7 @@ __device__ inline void b_compute(const typename BAccess<T, VECTOR>::Raw& rdy,
 template <typename T, bool VECTOR, int R>
 __global__ __launch_bounds__(256) void b_stage_kernel(const T* dy, const T* g, const T* fc, T* dg,
                                                       T* dfc, float* part, int64_t M, int64_t N,
-                                                      int64_t cv, int64_t rows, int txlog2) {
+                                                      int64_t cv, int64_t nunits, int txlog2) {
   using A = BAccess<T, VECTOR>;
   constexpr int V = A::V;
   const int tid = threadIdx.x;
@@ -163,15 +167,15 @@ __global__ __launch_bounds__(256) void b_stage_kernel(const T* dy, const T* g, c
   const int tx = tid & (TX - 1);
   const int ty = tid >> txlog2;
   const int64_t c = (int64_t)blockIdx.x * TX + tx;
-  const int64_t r0 = (int64_t)blockIdx.y * rows;
-  const int64_t r1 = (r0 + rows < M) ? r0 + rows : M;
 
   float sg[V], sf[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) sg[e] = sf[e] = 0.0f;
 
-  if (c < cv) {
-    const int64_t col = c * V;
+  const int64_t col = c * V;
+  for (int64_t unit = blockIdx.y; c < cv && unit < nunits; unit += gridDim.y) {
+    const int64_t r0 = unit * kBUnitRows;
+    const int64_t r1 = (r0 + kBUnitRows < M) ? r0 + kBUnitRows : M;
     int64_t r = r0 + ty;
     for (; r + (R - 1) * TY < r1; r += R * TY) {
       typename A::Raw a[R], b[R], d[R];
@@ -257,23 +261,23 @@ static hipError_t b_stage_t(const BPlan& p, const void* dy, const void* g, const
                             float* part, hipStream_t stream) {
   int txlog2 = 0;
   while ((1 << txlog2) < p.tx) ++txlog2;
-  const dim3 grid((unsigned)p.nstrips, (unsigned)p.nchunks);
+  const dim3 grid((unsigned)p.nstrips, (unsigned)p.nwalk);
   const T* a = static_cast<const T*>(dy);
   const T* b = static_cast<const T*>(g);
   const T* c = static_cast<const T*>(fc);
   if (p.vec > 1) {
     hipLaunchKernelGGL((b_stage_kernel<T, true, kBRowsInFlight>), grid, dim3(256), 0, stream, a, b, c,
-                       static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.rows,
+                       static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.nunits,
                        txlog2);
   } else {
     hipLaunchKernelGGL((b_stage_kernel<T, false, 1>), grid, dim3(256), 0, stream, a, b, c,
-                       static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.rows,
+                       static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.nunits,
                        txlog2);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((db_finalize_kernel<T>), dim3((unsigned)ceil_div(2 * N, 16)), dim3(256), 0,
-                     stream, part, static_cast<T*>(db_g), static_cast<T*>(db_fc), N, p.nchunks);
+                     stream, part, static_cast<T*>(db_g), static_cast<T*>(db_fc), N, p.nwalk);
   return hipGetLastError();
 }
 

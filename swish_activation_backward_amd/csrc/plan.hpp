@@ -14,39 +14,41 @@ inline int vec_of(int dtype) { return 16 / elem_size(dtype); }
 
 // ---------------------------------------------------------------- b stage
 // A workgroup of 256 threads owns a strip of TX vector-columns (TX a power of two
-// <= 64) and a chunk of rows; TY = 256 / TX rows are in flight per step.  Each
-// chunk leaves one fp32 partial row [2N] (dg sums, then dfc sums) in the workspace,
-// which the finalize kernel sums in chunk order.
+// <= 64; TY = 256 / TX rows are in flight per step).  The rows are cut into units of
+// kBUnitRows; the workgroups of a strip ("walkers", grid.y of them) take the units
+// round-robin (walker w: units w, w + walkers, ...), a static assignment that keeps the
+// column sums run-to-run deterministic while every walker ends within one unit of the
+// others.  Each walker leaves one fp32 partial row [2N] (dg sums, then dfc sums) in the
+// workspace, which the finalize kernel sums in walker order.
 struct BPlan {
   int vec;             // elements per 16-byte access (1 when the scalar path is used)
   int tx, ty;          // thread layout inside the 256-thread workgroup
   int64_t cv;          // vector columns per row = N / vec
   int64_t nstrips;     // ceil(cv / tx)
-  int64_t nchunks;     // row chunks (grid.y)
-  int64_t rows;        // rows per chunk
-  size_t ws_bytes;     // nchunks * 2N * sizeof(float)
+  int64_t nunits;      // ceil(M / kBUnitRows)
+  int64_t nwalk;       // walkers per strip (grid.y) = partial rows
+  size_t ws_bytes;     // nwalk * 2N * sizeof(float)
 };
 
 constexpr int kBThreads = 256;
-constexpr int64_t kBTargetBlocks = 2048;
-constexpr int64_t kBMinRows = 32;
-constexpr int kBRowsInFlight = 4;   // rows whose loads a lane issues before computing
+constexpr int64_t kBUnitRows = 64;       // rows per work unit
+constexpr int64_t kBWalkBlocks = 1024;   // resident workgroups to aim for (all strips)
+constexpr int kBRowsInFlight = 4;        // rows whose loads a lane issues before computing
 
 inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
   BPlan p{};
-  // the chunking depends only on (M, N, dtype), never on pointer alignment
+  // the walker count depends only on (M, N, dtype), never on pointer alignment
   const int vref = vec_of(dtype);
   const int64_t cv_ref = (N % vref == 0) ? N / vref : N;
   int tx_ref = 1;
   while (tx_ref < 64 && tx_ref < cv_ref) tx_ref <<= 1;
   const int64_t strips_ref = ceil_div(cv_ref, tx_ref);
-  int64_t nchunks = ceil_div(kBTargetBlocks, strips_ref);
-  const int64_t max_chunks = ceil_div(M, kBMinRows);
-  if (nchunks > max_chunks) nchunks = max_chunks;
-  if (nchunks < 1) nchunks = 1;
-  p.rows = ceil_div(M, nchunks);
-  p.nchunks = M > 0 ? ceil_div(M, p.rows) : 0;
-  p.ws_bytes = (M > 0 && N > 0) ? (size_t)p.nchunks * (size_t)(2 * N) * sizeof(float) : 0;
+  p.nunits = M > 0 ? ceil_div(M, kBUnitRows) : 0;
+  int64_t nwalk = ceil_div(kBWalkBlocks, strips_ref);
+  if (nwalk > p.nunits) nwalk = p.nunits;
+  if (nwalk < 1) nwalk = 1;
+  p.nwalk = nwalk;
+  p.ws_bytes = (M > 0 && N > 0) ? (size_t)p.nwalk * (size_t)(2 * N) * sizeof(float) : 0;
 
   p.vec = (vector_path && N % vref == 0) ? vref : 1;
   p.cv = N / p.vec;
