@@ -252,6 +252,20 @@ __device__ inline void stage_mma(const FragSet<T>& f, f32x16 (&acc)[FP][FQ]) {
     step_schedule<READS_PER_STEP>();                                      \
   } while (0)
 
+// The last step of a tile: as SWG_PIPE_STEP with u = 3, but the next tile's first stage
+// (slot 0) is read only after the epilogue, so that no operand fragments are live while
+// the accumulators are written out.
+#define SWG_PIPE_LAST_STEP(ISSUE_AHEAD, frags)                            \
+  do {                                                                    \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));            \
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                \
+    SWG_COMPILER_FENCE();                                                 \
+    __builtin_amdgcn_s_barrier();                                         \
+    SWG_COMPILER_FENCE();                                                 \
+    ISSUE_AHEAD(ring + 3 * SLOT);                                         \
+    stage_mma<T>(frags[1], acc);                                          \
+  } while (0)
+
 // Swap a value with the neighbouring lane (lane ^ 1): DPP quad_perm [1, 0, 3, 2].
 __device__ inline float swap_adjacent(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -285,7 +299,10 @@ template <> __device__ inline float2 unpack2<fp16>(uint32_t v) {
 // lanes (row R + 1, columns c - 1, c).  fn(row, col, lo, hi) gets tile-local
 // coordinates (row, col even).
 template <typename Fn>
-__device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane, Fn&& fn) {
+__device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane_in, Fn&& fn) {
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));   // per-lane terms are formed here, not hoisted out of the
+                                   // tile loop (they would stay live, and spill)
   const int odd = lane & 1;
 #pragma unroll
   for (int i = 0; i < FP; ++i)
@@ -302,14 +319,50 @@ __device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane, Fn&&
       }
 }
 
-// One tile's run of the ring: nst stages (a multiple of 4).  The issue side runs four
-// stages ahead and the LDS reads one stage ahead, so the last four issues of a tile fetch
-// the first stages of the next tile (`nxt_ctx`) and its last step reads the next tile's
-// first stage; keeping that hand-over in a peeled last round leaves the steady-state
+// Tile store straight from the accumulators: every lane pair turns its two rows x two
+// columns into one row each (pack to 16 bits, swap the packed words with the neighbouring
+// lane, byte-permute: even lanes keep row R, odd lanes row R + 1) and writes 32 bits per
+// row.  `r` is a buffer window over the tile's valid rows only, so stores to rows past the
+// output are dropped by the hardware range check; columns are checked only when the tile
+// is cut by the output's right edge (cols_left < 256: columns left from the tile's first;
+// a multiple of 8, so a pair never straddles it).  wrow0 / wcol0: the wave's first row /
+// column inside the tile.  All offsets are 32-bit (256 rows x 2^23 bytes < 2^31).
+template <typename T>
+__device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
+                                       __amdgpu_buffer_rsrc_t r, uint32_t row_bytes, int wrow0,
+                                       int wcol0, int cols_left) {
+  const int odd = lane & 1;
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;   // odd: (nb.hi, own.hi)
+  uint32_t loff = (uint32_t)(4 * (lane >> 5) + odd) * row_bytes +
+                  (uint32_t)(wcol0 + ((lane & 31) & ~1)) * 2u;
+  asm volatile("" : "+v"(loff));   // keeps the 32 row offsets below from being hoisted out of
+                                   // the tile loop (they would stay live, and spill)
+#pragma unroll
+  for (int i = 0; i < FP; ++i)
+#pragma unroll
+    for (int rr = 0; rr < 16; rr += 2) {
+      const uint32_t voff = loff + (uint32_t)(wrow0 + i * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes;
+#pragma unroll
+      for (int j = 0; j < FQ; ++j) {
+        const uint32_t own = pack2<T>(acc[i][j][rr], acc[i][j][rr + 1]);
+        const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
+        const uint32_t out = __builtin_amdgcn_perm(nb, own, sel);
+        if (cols_left >= BQ || wcol0 + j * 32 + ((lane & 31) & ~1) < cols_left)
+          __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)(voff + 64u * j), 0, 0);
+      }
+    }
+}
+
+// One tile's run of the ring: nst stages (a multiple of 4).  On entry the tile's first
+// stage has landed in slot 0 for every wave (the previous barrier says so); it is read
+// into fragment set 0 first.  The issue side runs four stages ahead and the LDS reads one
+// stage ahead, so the last four issues of a tile fetch the first stages of the next tile
+// (`nxt_ctx`); keeping that hand-over in a peeled last round leaves the steady-state
 // rounds free of branches.
 #define SWG_TILE_ROUNDS(ISSUE, READ, frags, cur_ctx, nxt_ctx, nst)                             \
   do {                                                                                     \
     int64_t t_ = 0;                                                                        \
+    READ(ring, frags[0]);                                                                  \
     for (; t_ + 4 < (nst); t_ += 4) {                                                      \
       SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 4, sl); }, READ, frags, 0);     \
       SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 5, sl); }, READ, frags, 1);     \
@@ -319,12 +372,12 @@ __device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane, Fn&&
     SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 0, sl); }, READ, frags, 0);            \
     SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 1, sl); }, READ, frags, 1);            \
     SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 2, sl); }, READ, frags, 2);            \
-    SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 3, sl); }, READ, frags, 3);            \
+    SWG_PIPE_LAST_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 3, sl); }, frags);                \
   } while (0)
 
-// Pipeline start: the first four stages of the first tile in flight, the first stage's
-// fragments in registers (set 0).
-#define SWG_PIPE_PROLOGUE(ISSUE, READ, frags, ctx)                 \
+// Pipeline start: the first four stages of the first tile in flight, the first stage
+// landed for every wave.
+#define SWG_PIPE_PROLOGUE(ISSUE, ctx)                              \
   do {                                                             \
     ISSUE(ctx, 0, ring);                                           \
     ISSUE(ctx, 1, ring + SLOT);                                    \
@@ -334,7 +387,6 @@ __device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane, Fn&&
     SWG_COMPILER_FENCE();                                          \
     __builtin_amdgcn_s_barrier();                                  \
     SWG_COMPILER_FENCE();                                          \
-    READ(ring, frags[0]);                                          \
   } while (0)
 
 // ----------------------------------------------------------------- x stage (NT)
@@ -384,7 +436,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   }
   auto issue = [&](const XTile& c, int64_t s, uint16_t* slot) {
     const bool hi = s >= sN;
-    const int64_t col0 = (hi ? s - sN : s) * BR;
+    int col0 = (int)(hi ? s - sN : s) * BR;
+    // opaque to the optimizer: the next tile's first issues would otherwise repeat the
+    // prologue's offsets, which it then keeps live (and spills) across the whole kernel
+    asm volatile("" : "+s"(col0));
     const int rows_a = c.live ? ((int)M - c.p0 < BP ? (int)M - c.p0 : BP) : 0;
     const int rows_b = c.live ? ((int)K - c.q0 < BQ ? (int)K - c.q0 : BQ) : 0;
     const __amdgpu_buffer_rsrc_t ra =
@@ -395,8 +450,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     uint32_t off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t col = col0 + lcol[i];
-      off[i] = col < N ? roff[i] + (uint32_t)(col * 2) : kOOB;
+      const int col = col0 + lcol[i];
+      off[i] = col < (int)N ? roff[i] + (uint32_t)(col * 2) : kOOB;
     }
     dma16<0 * 16 * BR * 2>(ra, off[0], dst);
     dma16<1 * 16 * BR * 2>(ra, off[1], dst);
@@ -414,17 +469,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   f32x16 acc[FP][FQ];
   FragSet<T> frags[2];
   XTile cur = x_tile(f0, my_tiles > 0, nq);
-  SWG_PIPE_PROLOGUE(X_ISSUE, X_READ, frags, cur);
+  SWG_PIPE_PROLOGUE(X_ISSUE, cur);
   for (int64_t j = 0; j < my_tiles; ++j) {
     const XTile nxt = x_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
     zero_acc(acc);
     SWG_TILE_ROUNDS(X_ISSUE, X_READ, frags, cur, nxt, nst);
     // epilogue: straight from the accumulators, two adjacent columns per 32-bit store
-    const int64_t p0 = (int64_t)cur.p0 + wp * 128, q0 = (int64_t)cur.q0 + wq * 128;
-    for_each_pair(acc, lane, [&](int row, int col, float lo, float hi) {
-      const int64_t p = p0 + row, q = q0 + col;
-      if (p < M && q < K) *reinterpret_cast<uint32_t*>(dx + p * K + q) = pack2<T>(lo, hi);
-    });
+    {
+      const int rows = (int)M - cur.p0 < BP ? (int)M - cur.p0 : BP;
+      store_tile_rows<T>(acc, lane,
+                         make_rsrc(dx + (int64_t)cur.p0 * K + cur.q0, clamp_bytes(rows, K * 2)),
+                         (uint32_t)(K * 2), wp * 128, wq * 128, (int)K - cur.q0);
+    }
     cur = nxt;
   }
 #undef X_ISSUE
@@ -473,7 +529,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
   // A 1 KiB load covers 2 rows x 32 chunks; this wave's loads are rows 8 wave + 2 i +
   // lane / 32 (i = 0..3) of A and of B, logical chunk (lane % 32) ^ wsw(row).  The lane
-  // parts of the offsets are fixed; the tile adds k0 / n0 (uniform).
+  // parts of the offsets are fixed; the tile adds k0 / n0 (uniform).  One buffer window
+  // per stage: rows m0 .. m0 + 32 (rows past m_end, and every row of a dead item, read 0).
   uint32_t xbase[4], dbase[4];
   int lcol[4];
 #pragma unroll
@@ -483,10 +540,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     xbase[i] = (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)lcol[i] * 2u;
     dbase[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)lcol[i] * 2u;
   }
-  // one buffer window per stage: rows m0 .. m0 + 32 (rows past m_end, and every row of
-  // a dead item, read 0)
   auto issue = [&](const WItem& w, int64_t st, uint16_t* slot) {
-    const int m0 = w.m_begin + (int)st * BR;
+    int m0 = w.m_begin + (int)st * BR;
+    asm volatile("" : "+s"(m0));   // keep per-stage offsets from being hoisted (see x stage)
     const int rows = w.live ? ((w.m_end - m0 < BR) ? w.m_end - m0 : BR) : 0;
     const int64_t mb = rows > 0 ? m0 : 0;
     const T* d = w.hi ? dfc : dg;
@@ -519,7 +575,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   f32x16 acc[FP][FQ];
   FragSet<T> frags[2];
   WItem cur = w_item(f0, my_items > 0, tiles, tnh, split_rows, M);
-  SWG_PIPE_PROLOGUE(W_ISSUE, W_READ, frags, cur);
+  SWG_PIPE_PROLOGUE(W_ISSUE, cur);
   const int64_t R2 = 2 * N;
   for (int64_t j = 0; j < my_items; ++j) {
     const WItem nxt = w_item(f0 + (j + 1) * G, j + 1 < my_items, tiles, tnh, split_rows, M);
