@@ -31,7 +31,7 @@ struct BPlan {
 };
 
 constexpr int kBThreads = 256;
-constexpr int64_t kBUnitRows = 64;       // rows per work unit
+constexpr int64_t kBUnitRows = 32;       // rows per work unit
 constexpr int64_t kBWalkBlocks = 1024;   // resident workgroups to aim for (all strips)
 constexpr int kBRowsInFlight = 4;        // rows whose loads a lane issues before computing
 
