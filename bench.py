@@ -13,6 +13,9 @@ over 8 TB/s (HBM) or its flops over 2.5 PFLOP/s (dense bf16 MFMA), whichever is 
 Each stage's absolute GB/s or TFLOP/s is listed too.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Defaults: 5 warm-up steps, 50 timed steps; per stage the mean (us), median, min and max
+of the per-step event times are reported.
 """
 from __future__ import annotations
 
@@ -153,8 +156,8 @@ def _cpu_model():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ffn_220k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -239,11 +242,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_stage = {n: 0.0 for n in names}
-    for ev in events:
-        for i, n in enumerate(names):
-            per_stage[n] += ev[i].elapsed_time(ev[i + 1]) * 1e-3
-    per_stage = {n: v / args.steps for n, v in per_stage.items()}
+    samples = {n: [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for ev in events]
+               for i, n in enumerate(names)}
+    per_stage = {n: sum(v) / len(v) for n, v in samples.items()}
     step_s = sum(per_stage.values())
     work = stage_work(M, K, N, L)
     t_roof = sum(v["t_roof"] for v in work.values())
@@ -252,7 +253,11 @@ def main():
     for n in names:
         t = per_stage[n]
         wk = work[n]
-        e = {"us": round(t * 1e6, 2), "GB/s": round(wk["bytes"] / t / 1e9, 1),
+        srt = sorted(samples[n])
+        e = {"us": round(t * 1e6, 2),
+             "median_us": round(srt[len(srt) // 2] * 1e6, 2),
+             "min_us": round(srt[0] * 1e6, 2), "max_us": round(srt[-1] * 1e6, 2),
+             "GB/s": round(wk["bytes"] / t / 1e9, 1),
              "bound": wk["bound"], "roofline_us": round(wk["t_roof"] * 1e6, 2),
              "frac": round(wk["t_roof"] / t, 4),
              "kernels": KERNELS["swish_grad" if n.startswith("swish") else n]}
