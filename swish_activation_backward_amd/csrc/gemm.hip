@@ -123,9 +123,11 @@ __device__ inline void zero_acc(f32x16 (&acc)[FP][FQ]) {
 
 // ------------------------------------------------------------------ x-stage tiles
 // Slot layout: [256 rows of A][32] then [256 rows of B][32]; a row is 4 chunks of 16 B.
-// Chunk c of row r sits at position c ^ xsw(r): for any 8 consecutive rows, and any 16,
-// the 16-byte reads of one MFMA operand land on distinct banks.
-__device__ inline int xsw(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Chunk c of row r sits at position c ^ xsw(r), xsw(r) = (r / 4) % 4: within 16
+// consecutive rows (one group of 16 lanes of a 16-byte read) the four rows that share a
+// 64-byte bank window take four different chunks (measured: full LDS read rate, no bank
+// conflict cycles).
+__device__ inline int xsw(int r) { return (r >> 2) & 3; }
 
 // Scheduling hint for one pipeline step: the LDS reads of the next stage (READS of them)
 // spread evenly between the 32 MFMAs of the current stage.  sched_group_barrier(mask, n,
