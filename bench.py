@@ -93,6 +93,28 @@ def recorded_traffic(workload, kernel):
     return rec.get("hbm_bytes_per_launch")
 
 
+def time_forward(swg, d, M, K, N, warmup, steps):
+    """The SwiGLU forward entry point (g, fc, y from x, W, b) at the same shape, timed on
+    its own after the step (it is not part of the backward step or of `value`)."""
+    import torch
+    g, fc, y = (torch.empty(M, N, dtype=torch.bfloat16, device=d["x"].device) for _ in range(3))
+    args = (d["x"], d["w_g"], d["w_fc"], d["b_g"], d["b_fc"], g, fc, y)
+    for _ in range(warmup):
+        swg.swiglu_fwd(*args)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        swg.swiglu_fwd(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    flops = 4.0 * M * K * N
+    return {"us": round(t * 1e6, 2), "TFLOP/s": round(flops / t / 1e12, 1),
+            "frac": round(flops / MFMA_BF16_PEAK / t, 4), "kernels": ["fwd_kernel"],
+            "note": "SwiGLU forward (g, fc, y), timed separately; not part of the step"}
+
+
 def copy_calibration(nbytes, reps=5):
     """A plain device-to-device copy of `nbytes`, for scaling the HBM byte counters."""
     import torch
@@ -299,6 +321,7 @@ def main():
         "stages": stages,
         "roofline": roof,
     }
+    out["forward"] = time_forward(swg, d, M, K, N, args.warmup, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, sw_inputs, args.cpu_rows, args.cpu_swish_len)
     print(json.dumps(out), flush=True)

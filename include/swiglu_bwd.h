@@ -107,6 +107,24 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
                         void* stream);
 
 /*
+ * SwiGLU forward [SwiGLU page, operator background: the function the three stages above
+ * differentiate]:
+ *   g[m,n]  = sum_k x[m,k] W_g[k,n]  + b_g[n]
+ *   fc[m,n] = sum_k x[m,k] W_fc[k,n] + b_fc[n]
+ *   y[m,n]  = SiLU(g[m,n]) * fc[m,n] = g sigma(g) fc
+ * x: [M, K]; w_g, w_fc: [K, N]; b_g, b_fc: [N], or NULL for no bias; g, fc, y: [M, N],
+ * OVERWRITTEN (g and fc are what swiglu_bwd_b takes).  dtype: bf16 or fp16 (fp32 returns
+ * SWG_ERR_UNSUPPORTED); K and N multiples of 8 and below 2^22, M below 2^31, else
+ * SWG_ERR_UNSUPPORTED.  Products on the matrix cores with fp32 accumulation; the bias is
+ * added in fp32; y is formed from the fp32 values of g and fc (before their rounding); each
+ * output is rounded once.  K = 0 gives g = b_g, fc = b_fc (the empty sums); x, w_g and
+ * w_fc may then be NULL.  No aliasing between any two buffers.
+ */
+swg_status swiglu_fwd(const void* x, const void* w_g, const void* w_fc,
+                      const void* b_g, const void* b_fc, void* g, void* fc, void* y,
+                      int64_t M, int64_t K, int64_t N, swg_dtype dtype, void* stream);
+
+/*
  * Swish gradient with a scalar beta [Swish page, sections 1.2 and 2.4]:
  *   t = beta * x,  s = sigma(t),  grad_x = grad * s * (1 + t * (1 - s))
  * grad, x, grad_x: n elements of one dtype (bf16, fp16 or fp32).  `beta` points to a

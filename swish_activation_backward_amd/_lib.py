@@ -14,7 +14,7 @@ import threading
 import torch
 
 __all__ = ["SwgError", "load_library", "library_path", "swish_grad", "swiglu_bwd_b",
-           "swiglu_bwd_w", "swiglu_bwd_x", "swiglu_bwd_b_workspace_size",
+           "swiglu_bwd_w", "swiglu_bwd_x", "swiglu_fwd", "swiglu_bwd_b_workspace_size",
            "swiglu_bwd_w_workspace_size", "swg_version", "DTYPE_CODE", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,8 @@ def load_library():
         lib.swiglu_bwd_w_workspace_size.restype = sz
         lib.swiglu_bwd_x.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
         lib.swiglu_bwd_x.restype = i32
+        lib.swiglu_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+        lib.swiglu_fwd.restype = i32
         lib.swg_status_string.argtypes = [i32]
         lib.swg_status_string.restype = ctypes.c_char_p
         lib.swg_last_hip_error.argtypes = []
@@ -208,3 +210,24 @@ def swiglu_bwd_x(dg, dfc, w_g, w_fc, dx, stream=None):
     st = lib.swiglu_bwd_x(_ptr(dg), _ptr(dfc), _ptr(w_g), _ptr(w_fc), _ptr(dx), M, K, N,
                           _dtype_code(dg), _stream(stream))
     _check("swiglu_bwd_x", st, lib)
+
+
+def swiglu_fwd(x, w_g, w_fc, b_g, b_fc, g, fc, y, stream=None):
+    """SwiGLU forward: g = x W_g + b_g, fc = x W_fc + b_fc, y = SiLU(g) fc (all three
+    [M, N] outputs overwritten).  ``b_g`` / ``b_fc`` may be None (no bias)."""
+    lib = load_library()
+    if x.dim() != 2 or w_g.dim() != 2:
+        raise ValueError("x must be [M, K] and w_g [K, N]")
+    M, K = x.shape
+    N = w_g.shape[1]
+    dt, dev = x.dtype, x.device
+    for name, t in (("w_g", w_g), ("w_fc", w_fc)):
+        _dense(name, t, dt, (K, N), dev)
+    for name, t in (("b_g", b_g), ("b_fc", b_fc)):
+        if t is not None:
+            _dense(name, t, dt, (N,), dev)
+    for name, t in (("g", g), ("fc", fc), ("y", y)):
+        _dense(name, t, dt, (M, N), dev)
+    st = lib.swiglu_fwd(_ptr(x), _ptr(w_g), _ptr(w_fc), _ptr(b_g), _ptr(b_fc), _ptr(g),
+                        _ptr(fc), _ptr(y), M, K, N, _dtype_code(x), _stream(stream))
+    _check("swiglu_fwd", st, lib)

@@ -135,11 +135,14 @@ __device__ inline int xsw(int r) { return (r >> 2) & 3; }
 #define SWG_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 template <int READS>
 __device__ inline void step_schedule() {
-  constexpr int kMfmaPerRead = 32 / READS;
+  static_assert(READS == 16 || READS == 24 || READS == 32, "reads per step");
+  // groups of (MFMAs, reads) that cover 32 MFMAs and READS reads evenly
+  constexpr int kGroups = READS == 24 ? 8 : READS;
+  constexpr int kMfma = 32 / kGroups, kReads = READS / kGroups;
 #pragma unroll
-  for (int q = 0; q < READS; ++q) {
-    SWG_SCHED(0x008, kMfmaPerRead);
-    SWG_SCHED(0x100, 1);
+  for (int q = 0; q < kGroups; ++q) {
+    SWG_SCHED(0x008, kMfma);
+    SWG_SCHED(0x100, kReads);
   }
 }
 
@@ -637,6 +640,202 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, int64_t wor
     p[i] = 0u;
 }
 
+// ----------------------------------------------------------------- forward (NN)
+// SwiGLU forward [SwiGLU page, operator background]: g = x W_g + b_g, fc = x W_fc + b_fc,
+// y = SiLU(g) fc, one GEMM [M, K] x [K, 2N] with a fused epilogue.  A = x rows m,
+// contraction k contiguous (the x stage's operand A layout); B = W_g | W_fc rows k,
+// columns n contiguous (the w stage's operand B layout, read with transposing reads).
+// A workgroup owns 256 rows x 128 columns of g AND the same 128 columns of fc, so the
+// epilogue has both at hand; each wave 128 rows x 64 columns of each (4 x 2 + 4 x 2 MFMA
+// tiles: 256 accumulators, as in the backward GEMMs).  Slot layout: [256 rows of x][32]
+// then [32 k-rows of W_g][128] then [32 k-rows of W_fc][128] (32 KiB).
+constexpr int FN = 128;   // output columns of g (and of fc) per tile
+
+// transposing-read fragment of 16 contraction rows from a [k][RL] tile (see w_frag)
+template <typename T, int RL>
+__device__ inline typename Mfma<T>::frag tr_frag(const uint16_t* p) {
+  const i16x4 lo = tr_read(p);
+  const i16x4 hi = tr_read(p + 4 * RL);
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(typename Mfma<T>::frag, v);
+}
+
+struct FTile {   // first row of x / of the outputs, first column of W / of the outputs
+  int p0, n0;
+  bool live;
+};
+
+__device__ inline FTile f_tile(int64_t L, bool live, int64_t nn) {
+  FTile c;
+  c.live = live;
+  const int64_t LL = live ? L : 0;
+  c.p0 = (int)(LL / nn) * BP;
+  c.n0 = (int)(LL % nn) * FN;
+  return c;
+}
+
+template <typename T>
+__device__ inline void f_read(const uint16_t* slot, int wp, int lane, const int (&boff)[2],
+                              FragSet<T>& f) {
+  using F = typename Mfma<T>::frag;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int lc = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FP; ++i) {
+      const int r = wp * 128 + i * 32 + (lane & 31);
+      f.a[kk][i] = *reinterpret_cast<const F*>(slot + r * BR + ((lc ^ xsw(r)) << 3));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f.b[kk][j] = tr_frag<T, FN>(slot + BP * BR + 16 * kk * FN + boff[j]);
+      f.b[kk][2 + j] = tr_frag<T, FN>(slot + BP * BR + BR * FN + 16 * kk * FN + boff[j]);
+    }
+  }
+}
+
+// Store one output of the epilogue: values v0 (row R) and v1 (row R + 1) of one column per
+// lane become 32-bit row pairs exactly as in store_tile_rows.
+template <typename T>
+__device__ inline void f_store_pair(float v0, float v1, uint32_t sel, __amdgpu_buffer_rsrc_t r,
+                                    uint32_t voff, bool ok) {
+  const uint32_t own = pack2<T>(v0, v1);
+  const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
+  const uint32_t out = __builtin_amdgcn_perm(nb, own, sel);
+  if (ok) __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)voff, 0, 0);
+}
+
+template <typename T>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_kernel(
+    const T* __restrict__ x, const T* __restrict__ wg, const T* __restrict__ wfc,
+    const T* __restrict__ bg, const T* __restrict__ bfc, T* __restrict__ g, T* __restrict__ fc,
+    T* __restrict__ y, int64_t M, int64_t K, int64_t N, int64_t nn, int64_t ntiles) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[4 * SLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wp = wave / WQ, wq = wave % WQ;
+  const int64_t G = gridDim.x;
+  const int64_t f0 = xcd_remap(blockIdx.x, G);
+  const int64_t my_tiles = ntiles > f0 ? (ntiles - f0 + G - 1) / G : 0;
+  int64_t nst = 4 * ((K + 4 * BR - 1) / (4 * BR));   // whole ring rounds (K = 0: one round
+  if (nst < 4) nst = 4;                                  // of zeros, outputs = bias terms)
+
+  // x: a 1 KiB load covers 16 rows x 4 chunks (rows 64 wave + 16 i + lane / 4), as in the
+  // x stage.  W: a 1 KiB load covers 4 k-rows x 16 chunks (rows 8 wave + 4 t + lane / 16),
+  // logical chunk (lane % 16) ^ wsw(row).
+  uint32_t roff[4];
+  int lcol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 64 * wave + 16 * i + (lane >> 2);
+    roff[i] = (uint32_t)row * (uint32_t)(K * 2);
+    lcol[i] = ((lane & 3) ^ xsw(row)) * 8;
+  }
+  uint32_t wbase[2];
+  int wcol[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = 8 * wave + 4 * t + (lane >> 4);
+    wcol[t] = ((lane & 15) ^ wsw(row)) * 8;
+    wbase[t] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)wcol[t] * 2u;
+  }
+  auto issue = [&](const FTile& c, int64_t st, uint16_t* slot) {
+    int k0 = (int)st * BR;
+    asm volatile("" : "+s"(k0));   // keep per-stage offsets from being hoisted (x stage)
+    const int rows_a = c.live ? ((int)M - c.p0 < BP ? (int)M - c.p0 : BP) : 0;
+    const int rows_w = c.live ? ((int)K - k0 < BR ? (int)K - k0 : BR) : 0;
+    const int64_t kb = rows_w > 0 ? k0 : 0;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(x + (int64_t)c.p0 * K, clamp_bytes(rows_a, K * 2));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(wg + kb * N, clamp_bytes(rows_w, N * 2));
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(wfc + kb * N, clamp_bytes(rows_w, N * 2));
+    uint32_t off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = k0 + lcol[i];
+      off[i] = col < (int)K ? roff[i] + (uint32_t)(col * 2) : kOOB;
+    }
+    const int nleft = (int)N - c.n0;
+    const uint32_t n2 = (uint32_t)c.n0 * 2u;
+    const uint32_t wo0 = wcol[0] < nleft ? wbase[0] + n2 : kOOB;
+    const uint32_t wo1 = wcol[1] < nleft ? wbase[1] + n2 : kOOB;
+    const uint16_t* dst = slot + 64 * wave * BR;
+    const uint16_t* dstw = slot + BP * BR + 8 * wave * FN;
+    dma16<0 * 16 * BR * 2>(ra, off[0], dst);
+    dma16<1 * 16 * BR * 2>(ra, off[1], dst);
+    dma16<2 * 16 * BR * 2>(ra, off[2], dst);
+    dma16<3 * 16 * BR * 2>(ra, off[3], dst);
+    dma16<0 * 4 * FN * 2>(rg, wo0, dstw);
+    dma16<1 * 4 * FN * 2>(rg, wo1, dstw);
+    dma16<BR * FN * 2 + 0 * 4 * FN * 2>(rf, wo0, dstw);
+    dma16<BR * FN * 2 + 1 * 4 * FN * 2>(rf, wo1, dstw);
+  };
+  // transposing-read offsets of this wave's two 32-column blocks (see w_lane_offsets)
+  int boff[2];
+  {
+    const int grp = lane >> 4, sl = lane & 15;
+    const int q = 2 * (grp & 1) + ((sl & 3) >> 1);
+    const int sw = wsw(sl >> 2);
+    const int row = 8 * (grp >> 1) + (sl >> 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      boff[j] = row * FN + (((4 * (2 * wq + j) + q) ^ sw) << 3) + 4 * (sl & 1);
+  }
+#define F_ISSUE(c, s, slot) issue((c), (s), (slot))
+#define F_READ(slot, f) f_read<T>((slot), wp, lane, boff, (f))
+  constexpr int READS_PER_STEP = 24;   // 8 ds_read_b128 + 16 ds_read_b64_tr_b16
+
+  f32x16 acc[FP][FQ];
+  FragSet<T> frags[2];
+  FTile cur = f_tile(f0, my_tiles > 0, nn);
+  SWG_PIPE_PROLOGUE(F_ISSUE, cur);
+  for (int64_t j = 0; j < my_tiles; ++j) {
+    const FTile nxt = f_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nn);
+    zero_acc(acc);
+    SWG_TILE_ROUNDS(F_ISSUE, F_READ, frags, cur, nxt, nst);
+    // epilogue: bias, SiLU, product, three outputs
+    {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int odd = ln & 1;
+      const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+      const int rows = (int)M - cur.p0 < BP ? (int)M - cur.p0 : BP;
+      const uint32_t bytes = clamp_bytes(rows, N * 2);
+      const int64_t base = (int64_t)cur.p0 * N + cur.n0;
+      const __amdgpu_buffer_rsrc_t rgo = make_rsrc(g + base, bytes);
+      const __amdgpu_buffer_rsrc_t rfo = make_rsrc(fc + base, bytes);
+      const __amdgpu_buffer_rsrc_t ryo = make_rsrc(y + base, bytes);
+      const int nleft = (int)N - cur.n0;
+      const uint32_t row_bytes = (uint32_t)(N * 2);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int colv = wq * 64 + jj * 32 + (ln & 31);          // this lane's column
+        const int colp = wq * 64 + jj * 32 + ((ln & 31) & ~1);   // its pair's first column
+        const bool okc = colp < nleft;
+        const float bgv = (bg != nullptr && colv < nleft) ? to_f32(bg[cur.n0 + colv]) : 0.0f;
+        const float bfv = (bfc != nullptr && colv < nleft) ? to_f32(bfc[cur.n0 + colv]) : 0.0f;
+        const uint32_t loff = (uint32_t)(4 * (ln >> 5) + odd) * row_bytes + (uint32_t)colp * 2u;
+#pragma unroll
+        for (int i = 0; i < FP; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 16; rr += 2) {
+            const uint32_t voff =
+                loff + (uint32_t)(wp * 128 + i * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes;
+            const float g0 = acc[i][jj][rr] + bgv, g1 = acc[i][jj][rr + 1] + bgv;
+            const float c0 = acc[i][2 + jj][rr] + bfv, c1 = acc[i][2 + jj][rr + 1] + bfv;
+            const SigmoidParts s0 = sigmoid_parts(g0), s1 = sigmoid_parts(g1);
+            f_store_pair<T>(g0, g1, sel, rgo, voff, okc);
+            f_store_pair<T>(c0, c1, sel, rfo, voff, okc);
+            f_store_pair<T>(g0 * s0.s * c0, g1 * s1.s * c1, sel, ryo, voff, okc);
+          }
+      }
+    }
+    cur = nxt;
+  }
+#undef F_ISSUE
+#undef F_READ
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+}
+
 template <typename T>
 static hipError_t x_stage_t(const void* dg, const void* dfc, const void* wg, const void* wfc,
                             void* dx, int64_t M, int64_t K, int64_t N, int cus,
@@ -683,6 +882,28 @@ hipError_t launch_w_stage(int dtype, const WPlan& p, const void* x, const void* 
                           int64_t N, float* ws, int cus, hipStream_t stream) {
   if (dtype == 0) return w_stage_t<bf16>(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, cus, stream);
   return w_stage_t<fp16>(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, cus, stream);
+}
+
+template <typename T>
+static hipError_t fwd_t(const void* x, const void* wg, const void* wfc, const void* bg,
+                        const void* bfc, void* g, void* fc, void* y, int64_t M, int64_t K,
+                        int64_t N, int cus, hipStream_t stream) {
+  const int64_t np = ceil_div(M, BP), nn = ceil_div(N, FN);
+  const int64_t ntiles = np * nn;
+  const int64_t grid = ntiles < cus ? ntiles : cus;
+  hipLaunchKernelGGL((fwd_kernel<T>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                     static_cast<const T*>(x), static_cast<const T*>(wg),
+                     static_cast<const T*>(wfc), static_cast<const T*>(bg),
+                     static_cast<const T*>(bfc), static_cast<T*>(g), static_cast<T*>(fc),
+                     static_cast<T*>(y), M, K, N, nn, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(int dtype, const void* x, const void* w_g, const void* w_fc,
+                      const void* b_g, const void* b_fc, void* g, void* fc, void* y, int64_t M,
+                      int64_t K, int64_t N, int cus, hipStream_t stream) {
+  if (dtype == 0) return fwd_t<bf16>(x, w_g, w_fc, b_g, b_fc, g, fc, y, M, K, N, cus, stream);
+  return fwd_t<fp16>(x, w_g, w_fc, b_g, b_fc, g, fc, y, M, K, N, cus, stream);
 }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {

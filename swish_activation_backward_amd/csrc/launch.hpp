@@ -27,6 +27,12 @@ hipError_t launch_x_stage(int dtype, const void* dg, const void* dfc, const void
                           const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
                           hipStream_t stream);
 
+// SwiGLU forward: g, fc, y [M, N] from x [M, K], W_g, W_fc [K, N], b_g, b_fc [N] (may be
+// null); one persistent workgroup per CU.
+hipError_t launch_fwd(int dtype, const void* x, const void* w_g, const void* w_fc,
+                      const void* b_g, const void* b_fc, void* g, void* fc, void* y, int64_t M,
+                      int64_t K, int64_t N, int cus, hipStream_t stream);
+
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace swg

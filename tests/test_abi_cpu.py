@@ -127,6 +127,26 @@ def test_gemm_argument_errors(lib):
     assert lib.swiglu_bwd_x(*xa(dg=ctypes.c_void_p(0x10008))) == UNSUPPORTED
 
 
+def test_forward_argument_errors(lib):
+    M, K, N = 4096, 64, 128
+    W_ = ctypes.c_void_p(0x80000)
+    fa = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                       (("x", P), ("wg", Q), ("wfc", R), ("bg", S), ("bfc", T), ("g", U),
+                        ("fc", V), ("y", W_), ("M", M), ("K", K), ("N", N), ("dt", BF16),
+                        ("s", NULL))]
+    assert lib.swiglu_fwd(*fa(M=0)) == OK
+    assert lib.swiglu_fwd(*fa(N=0)) == OK
+    assert lib.swiglu_fwd(*fa(M=-1)) == INVALID
+    assert lib.swiglu_fwd(*fa(dt=FP32)) == UNSUPPORTED
+    assert lib.swiglu_fwd(*fa(dt=7)) == INVALID
+    assert lib.swiglu_fwd(*fa(K=60)) == UNSUPPORTED
+    assert lib.swiglu_fwd(*fa(N=100)) == UNSUPPORTED
+    for k in ("x", "wg", "wfc", "g", "fc", "y"):
+        assert lib.swiglu_fwd(*fa(**{k: NULL})) == NULLPTR, k
+    assert lib.swiglu_fwd(*fa(x=ctypes.c_void_p(0x10008))) == UNSUPPORTED
+    assert lib.swiglu_fwd(*fa(bg=ctypes.c_void_p(0x40001))) == INVALID
+
+
 def test_workspace_queries():
     import torch
     b = swg.swiglu_bwd_b_workspace_size

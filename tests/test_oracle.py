@@ -275,6 +275,13 @@ def test_forward_ref_matches_definition():
     g, fc, y = R.swiglu_forward_ref(x, w_g, b_g, w_fc, b_fc)
     want = torch.nn.functional.silu(torch.tensor(x @ w_g + b_g)) * torch.tensor(x @ w_fc + b_fc)
     np.testing.assert_allclose(y, want.numpy(), rtol=1e-13)
+    # g and fc against the sums written out term by term
+    for m in range(4):
+        for n in range(5):
+            sg = b_g[n] + sum(x[m, k] * w_g[k, n] for k in range(3))
+            sf = b_fc[n] + sum(x[m, k] * w_fc[k, n] for k in range(3))
+            assert abs(g[m, n] - sg) <= 1e-12 * (1 + abs(sg))
+            assert abs(fc[m, n] - sf) <= 1e-12 * (1 + abs(sf))
     out = R.swiglu_bwd_ref(rng.normal(size=(4, 5)), x, w_g, w_fc, g, fc)
     assert set(out) == {"dg", "dfc", "db_g", "db_fc", "dw_g", "dw_fc", "dx"}
 
