@@ -79,7 +79,14 @@ def load_library():
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device pointer of a GPU tensor; host tensors are refused (the kernels would
+    dereference host addresses)."""
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError(f"tensor on {t.device}: the library computes on the GPU only "
+                         f"(move inputs and outputs to a cuda device)")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):

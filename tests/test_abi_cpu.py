@@ -173,6 +173,12 @@ def test_binding_checks_shapes_without_gpu():
         swg.swish_grad(x, torch.zeros(4, 9, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         swg.swiglu_bwd_x(x, x, torch.zeros(8, 8, dtype=torch.float16), x, x)
+    # well-formed host tensors are refused before any library call
+    with pytest.raises(ValueError, match="GPU only"):
+        swg.swish_grad(x, x)
+    w = torch.zeros(8, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU only"):
+        swg.swiglu_fwd(x, w, w, None, None, x.clone(), x.clone(), x.clone())
 
 
 def test_product_path_has_no_cpu_fallback():
