@@ -152,8 +152,23 @@ template <typename T> struct FragSet {
   typename Mfma<T>::frag a[2][FP], b[2][FQ];
 };
 
-template <typename T>
-__device__ inline void x_read(const uint16_t* slot, int wp, int wq, int lane, FragSet<T>& f) {
+// x-stage LDS: operand A (dg | dfc, streamed from HBM) moves 64 contraction elements
+// (128-byte row segments) per load, operand B (W, resident in L2) 32.  A ring: three slots
+// of [256 rows][64] (pipeline stage 2d + h is half h of A-stage d); B ring: four slots of
+// [256 rows][32].  A row of an A slot is 8 chunks of 16 B, chunk c of row r at position
+// c ^ xsw8(r): within 16 consecutive rows the pairs of rows that share a 256-byte bank
+// window take different chunks.
+constexpr int XA_BR = 2 * BR;                 // contraction elements per A stage
+constexpr int XA_SLOT = BP * XA_BR;           // elements per A slot (32 KiB)
+constexpr int XB_SLOT = BQ * BR;              // elements per B slot (16 KiB)
+constexpr int XA_LOADS = XA_SLOT * 2 / 1024 / (NT / 64);   // 1 KiB loads per wave: 8
+constexpr int XB_LOADS = XB_SLOT * 2 / 1024 / (NT / 64);   // 4
+__device__ inline int xsw8(int r) { return (r >> 1) & 7; }
+
+// Fragments of one pipeline stage: half HALF of the A slot, and the B slot.
+template <typename T, int HALF>
+__device__ inline void x_read(const uint16_t* aslot, const uint16_t* bslot, int wp, int wq,
+                              int lane, FragSet<T>& f) {
   using F = typename Mfma<T>::frag;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
@@ -161,15 +176,16 @@ __device__ inline void x_read(const uint16_t* slot, int wp, int wq, int lane, Fr
 #pragma unroll
     for (int i = 0; i < FP; ++i) {
       const int r = wp * 128 + i * 32 + (lane & 31);
-      f.a[kk][i] = *reinterpret_cast<const F*>(slot + r * BR + ((lc ^ xsw(r)) << 3));
+      f.a[kk][i] = *reinterpret_cast<const F*>(aslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
     }
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
       const int r = wq * 128 + j * 32 + (lane & 31);
-      f.b[kk][j] = *reinterpret_cast<const F*>(slot + (BP + r) * BR + ((lc ^ xsw(r)) << 3));
+      f.b[kk][j] = *reinterpret_cast<const F*>(bslot + r * BR + ((lc ^ xsw(r)) << 3));
     }
   }
 }
+
 // ------------------------------------------------------------------ w-stage tiles
 // Slot layout: [32 contraction rows of A][256] then [32 rows of B][256]; a row is 32
 // chunks of 16 B, chunk c of row m at position c ^ wsw(m).  A transposing read covers
@@ -343,7 +359,7 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
   asm volatile("" : "+v"(loff));   // keeps the 32 row offsets below from being hoisted out of
                                    // the tile loop (they would stay live, and spill)
 #pragma unroll
-  for (int i = 0; i < FP; ++i)
+  for (int i = 0; i < FP; ++i) {
 #pragma unroll
     for (int rr = 0; rr < 16; rr += 2) {
       const uint32_t voff = loff + (uint32_t)(wrow0 + i * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes;
@@ -356,6 +372,10 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
           __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)(voff + 64u * j), 0, 0);
       }
     }
+    // keep the scheduler from hoisting every accumulator read to the top (the copies
+    // would need more registers than the tile loop has free, and spill)
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // One tile's run of the ring: nst stages (a multiple of 4).  On entry the tile's first
@@ -395,10 +415,20 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
   } while (0)
 
 // ----------------------------------------------------------------- x stage (NT)
-// A = [dg | dfc] rows p (M), B = [W_g | W_fc] rows q (K).  Stage s < sN contracts over
-// columns 32 s .. of dg / W_g, stage s >= sN over the same columns of dfc / W_fc (sN is
-// rounded up to even so that a tile is a whole number of 4-stage ring rounds; the extra
-// stages read zeros).  Tile L covers rows (L / nq) * 256 and columns (L % nq) * 256.
+// A = [dg | dfc] rows p (M), B = [W_g | W_fc] rows q (K).  Pipeline stage s < sN contracts
+// over columns 32 s .. of dg / W_g, stage s >= sN over the same columns of dfc / W_fc
+// (sN = 2 max(2, ceil(N / 64)), so that A stage d = s / 2 never straddles dg and dfc;
+// columns past N read zeros).  Tile L covers rows (L / nq) * 256 and columns (L % nq) * 256.
+//
+// Step t of a tile (stages run four steps deep in B and, at odd steps, two A stages deep):
+//   wait until this wave's loads of B stage t + 1 and of A stage (t + 1) / 2 landed and its
+//   own LDS reads are done; barrier; issue B stage t + 4 into the B slot just consumed; at
+//   odd t = 2d + 1 also issue A stage d + 3 into the A slot of A stage d (both of its halves
+//   were read by now); read stage t + 1 into the other register set while the MFMAs run on
+//   stage t.  Every wave issues 4 B loads per step and 8 A loads per odd step, so "the
+//   stages needed next have landed" is "at most 24 (even t) / 16 (odd t) loads outstanding";
+//   the prologue issues in the same order (A0 B0 B1 A1 B2 B3 A2).  Issues past the tile's
+//   last stage fetch the next tile's first stages (uniform selects, no branch).
 struct XTile {   // first row of the dg/dfc panel and of the W panel; 32-bit (M < 2^31)
   int p0, q0;
   bool live;
@@ -418,67 +448,153 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const T* __restrict__ dg, const T* __restrict__ dfc, const T* __restrict__ wg,
     const T* __restrict__ wfc, T* __restrict__ dx, int64_t M, int64_t K, int64_t N, int64_t nq,
     int64_t ntiles) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[4 * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[3 * XA_SLOT + 4 * XB_SLOT];
+  uint16_t* const ra0 = ring;
+  uint16_t* const rb0 = ring + 3 * XA_SLOT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / WQ, wq = wave % WQ;
   const int64_t G = gridDim.x;
   const int64_t f0 = xcd_remap(blockIdx.x, G);
   const int64_t my_tiles = ntiles > f0 ? (ntiles - f0 + G - 1) / G : 0;
-  const int64_t sN = 2 * ((N + 2 * BR - 1) / (2 * BR));
-  const int64_t nst = 2 * sN;
+  // A stages per dg (or dfc) half, at least 2 so that a tile has at least 4: the A loads
+  // run up to three A stages ahead and must stay within the next tile
+  int sD = (int)((N + XA_BR - 1) / XA_BR);
+  if (sD < 2) sD = 2;
+  const int sN = 2 * sD;                           // pipeline stages per half
+  const int nst = 2 * sN;                          // pipeline stages per tile (multiple of 4)
+  const int nds = sN;                              // A stages per tile
 
-  // A 1 KiB load covers 16 rows x 4 chunks; this wave's loads are rows
-  // 64 wave + 16 i + lane / 4 (i = 0..3) of A and of B.  The lane fetches logical chunk
-  // (lane % 4) ^ xsw(row), so LDS position lane % 4 of the row holds it swizzled.
-  uint32_t roff[4];
-  int lcol[4];
+  // A: a 1 KiB load covers 8 rows x 8 chunks, rows 64 wave + 8 i + lane / 8 (i = 0..7);
+  // B: 16 rows x 4 chunks, rows 64 wave + 16 i + lane / 4 (i = 0..3).  The lane fetches
+  // the logical chunk that its LDS position holds under the swizzle.
+  // The swizzles depend only on (lane, i parity) for A and on the lane for B:
+  // xsw8(64 wave + 8 i + lane / 8) = (4 i + lane / 16) % 8, xsw(64 wave + 16 i + lane / 4) =
+  // (lane / 16) % 4; so the column terms take two values (A) and one (B) per lane.
+  uint32_t aoff[8], boff[4];
+  int acol[2];
+  acol[0] = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
+  acol[1] = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
+  const int bcol = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 64 * wave + 8 * i + (lane >> 3);
+    aoff[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)acol[i & 1] * 2u;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 64 * wave + 16 * i + (lane >> 2);
-    roff[i] = (uint32_t)row * (uint32_t)(N * 2);
-    lcol[i] = ((lane & 3) ^ xsw(row)) * 8;
+    boff[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)bcol * 2u;
   }
-  auto issue = [&](const XTile& c, int64_t s, uint16_t* slot) {
-    const bool hi = s >= sN;
-    int col0 = (int)(hi ? s - sN : s) * BR;
-    // opaque to the optimizer: the next tile's first issues would otherwise repeat the
-    // prologue's offsets, which it then keeps live (and spills) across the whole kernel
-    asm volatile("" : "+s"(col0));
-    const int rows_a = c.live ? ((int)M - c.p0 < BP ? (int)M - c.p0 : BP) : 0;
-    const int rows_b = c.live ? ((int)K - c.q0 < BQ ? (int)K - c.q0 : BQ) : 0;
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc((hi ? dfc : dg) + (int64_t)c.p0 * N, clamp_bytes(rows_a, N * 2));
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc((hi ? wfc : wg) + (int64_t)c.q0 * N, clamp_bytes(rows_b, N * 2));
-    const uint16_t* dst = slot + 64 * wave * BR;   // this wave's 4 rows-of-16 blocks
-    uint32_t off[4];
+  // A stage d of tile c (d >= nds: stage d - nds of tile n) into an A slot
+  auto issue_a = [&](const XTile& c, const XTile& n, int d, uint16_t* slot) {
+    asm volatile("" : "+s"(d));   // keep per-stage offsets from being hoisted (they would
+                                  // stay live across the tile loop, and spill)
+    const bool nx = d >= nds;
+    // value selects (no branch in the pipeline), pinned to scalar registers: the buffer
+    // window must be wave-uniform
+    const int p0 = __builtin_amdgcn_readfirstlane(nx ? n.p0 : c.p0);
+    const bool live = __builtin_amdgcn_readfirstlane((nx ? n.live : c.live) ? 1 : 0) != 0;
+    const int dd = nx ? d - nds : d;
+    const bool hi = dd >= sD;
+    const int col0 = (hi ? dd - sD : dd) * XA_BR;
+    const int rows = live ? ((int)M - p0 < BP ? (int)M - p0 : BP) : 0;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc((hi ? dfc : dg) + (int64_t)p0 * N, (uint32_t)rows * (uint32_t)(N * 2));
+    const uint16_t* dst = slot + 64 * wave * XA_BR;
+    uint32_t o[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = col0 + lcol[i];
-      off[i] = col < (int)N ? roff[i] + (uint32_t)(col * 2) : kOOB;
-    }
-    dma16<0 * 16 * BR * 2>(ra, off[0], dst);
-    dma16<1 * 16 * BR * 2>(ra, off[1], dst);
-    dma16<2 * 16 * BR * 2>(ra, off[2], dst);
-    dma16<3 * 16 * BR * 2>(ra, off[3], dst);
-    dma16<BP * BR * 2 + 0 * 16 * BR * 2>(rb, off[0], dst);
-    dma16<BP * BR * 2 + 1 * 16 * BR * 2>(rb, off[1], dst);
-    dma16<BP * BR * 2 + 2 * 16 * BR * 2>(rb, off[2], dst);
-    dma16<BP * BR * 2 + 3 * 16 * BR * 2>(rb, off[3], dst);
+    for (int i = 0; i < 8; ++i)
+      o[i] = col0 + acol[i & 1] < (int)N ? aoff[i] + (uint32_t)col0 * 2u : kOOB;
+    dma16<0 * 1024>(r, o[0], dst);
+    dma16<1 * 1024>(r, o[1], dst);
+    dma16<2 * 1024>(r, o[2], dst);
+    dma16<3 * 1024>(r, o[3], dst);
+    dma16<4 * 1024>(r, o[4], dst);
+    dma16<5 * 1024>(r, o[5], dst);
+    dma16<6 * 1024>(r, o[6], dst);
+    dma16<7 * 1024>(r, o[7], dst);
   };
-#define X_ISSUE(c, s, slot) issue((c), (s), (slot))
-#define X_READ(slot, f) x_read<T>((slot), wp, wq, lane, (f))
-  constexpr int READS_PER_STEP = 16;   // ds_read_b128: 8 per operand
+  // B stage s of tile c (s >= nst: stage s - nst of tile n) into a B slot
+  auto issue_b = [&](const XTile& c, const XTile& n, int s, uint16_t* slot) {
+    asm volatile("" : "+s"(s));
+    const bool nx = s >= nst;
+    const int q0 = __builtin_amdgcn_readfirstlane(nx ? n.q0 : c.q0);
+    const bool live = __builtin_amdgcn_readfirstlane((nx ? n.live : c.live) ? 1 : 0) != 0;
+    const int ss = nx ? s - nst : s;
+    const bool hi = ss >= sN;
+    const int col0 = (hi ? ss - sN : ss) * BR;
+    const int rows = live ? ((int)K - q0 < BQ ? (int)K - q0 : BQ) : 0;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc((hi ? wfc : wg) + (int64_t)q0 * N, (uint32_t)rows * (uint32_t)(N * 2));
+    const uint16_t* dst = slot + 64 * wave * BR;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = col0 + bcol < (int)N ? boff[i] + (uint32_t)col0 * 2u : kOOB;
+    dma16<0 * 16 * BR * 2>(r, o[0], dst);
+    dma16<1 * 16 * BR * 2>(r, o[1], dst);
+    dma16<2 * 16 * BR * 2>(r, o[2], dst);
+    dma16<3 * 16 * BR * 2>(r, o[3], dst);
+  };
+#define X_READ(h, as, bs, f) x_read<T, (h)>((as), (bs), wp, wq, lane, (f))
+  // one pipeline step u (= t mod 4) of a round starting at stage t0; `as` is the A slot of
+  // A stage t / 2; READ_NEXT = 0 on the last step of a tile
+#define X_STEP(u, READ_NEXT)                                                              \
+  do {                                                                                    \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(((u) & 1) ? 2 * XB_LOADS + XA_LOADS                \
+                                                  : 2 * XB_LOADS + 2 * XA_LOADS));        \
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                                \
+    SWG_COMPILER_FENCE();                                                                 \
+    __builtin_amdgcn_s_barrier();                                                         \
+    SWG_COMPILER_FENCE();                                                                 \
+    issue_b(cur, nxt, t0 + (u) + 4, rb0 + (u) * XB_SLOT);                                  \
+    if ((u) & 1) issue_a(cur, nxt, (t0 + (u)) / 2 + 3, ra0 + as * XA_SLOT);                \
+    if (READ_NEXT) {                                                                      \
+      if ((u) & 1) {                                                                      \
+        X_READ(0, ra0 + (as == 2 ? 0 : as + 1) * XA_SLOT, rb0 + (((u) + 1) & 3) * XB_SLOT,  \
+               frags[((u) + 1) & 1]);                                                     \
+      } else {                                                                            \
+        X_READ(1, ra0 + as * XA_SLOT, rb0 + (((u) + 1) & 3) * XB_SLOT, frags[((u) + 1) & 1]); \
+      }                                                                                   \
+    }                                                                                     \
+    stage_mma<T>(frags[(u) & 1], acc);                                                    \
+    if (READ_NEXT) step_schedule<16>();                                                   \
+    if ((u) & 1) as = (as == 2 ? 0 : as + 1);                                             \
+  } while (0)
 
   f32x16 acc[FP][FQ];
   FragSet<T> frags[2];
   XTile cur = x_tile(f0, my_tiles > 0, nq);
-  SWG_PIPE_PROLOGUE(X_ISSUE, cur);
+  XTile nxt = x_tile(f0 + G, my_tiles > 1, nq);
+  int as = 0;   // A slot of the A stage holding the current pipeline stage
+  // prologue, in the steady-state issue order: A0 B0 B1 A1 B2 B3 A2
+  issue_a(cur, nxt, 0, ra0);
+  issue_b(cur, nxt, 0, rb0);
+  issue_b(cur, nxt, 1, rb0 + XB_SLOT);
+  issue_a(cur, nxt, 1, ra0 + XA_SLOT);
+  issue_b(cur, nxt, 2, rb0 + 2 * XB_SLOT);
+  issue_b(cur, nxt, 3, rb0 + 3 * XB_SLOT);
+  issue_a(cur, nxt, 2, ra0 + 2 * XA_SLOT);
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * XB_LOADS + 2 * XA_LOADS));   // A0 and B0 landed
+  SWG_COMPILER_FENCE();
+  __builtin_amdgcn_s_barrier();
+  SWG_COMPILER_FENCE();
   for (int64_t j = 0; j < my_tiles; ++j) {
-    const XTile nxt = x_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
+    nxt = x_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
     zero_acc(acc);
-    SWG_TILE_ROUNDS(X_ISSUE, X_READ, frags, cur, nxt, nst);
+    X_READ(0, ra0 + as * XA_SLOT, rb0, frags[0]);   // stage 0 (A half 0, B slot 0)
+    int t0 = 0;
+    for (; t0 + 4 < nst; t0 += 4) {
+      X_STEP(0, 1);
+      X_STEP(1, 1);
+      X_STEP(2, 1);
+      X_STEP(3, 1);
+    }
+    X_STEP(0, 1);
+    X_STEP(1, 1);
+    X_STEP(2, 1);
+    X_STEP(3, 0);
     // epilogue: straight from the accumulators, two adjacent columns per 32-bit store
     {
       const int rows = (int)M - cur.p0 < BP ? (int)M - cur.p0 : BP;
@@ -488,7 +604,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
     cur = nxt;
   }
-#undef X_ISSUE
+#undef X_STEP
 #undef X_READ
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
