@@ -152,20 +152,20 @@ template <typename T> struct FragSet {
   typename Mfma<T>::frag a[2][FP], b[2][FQ];
 };
 
-// x-stage LDS: operand A (dg | dfc, streamed from HBM) moves 64 contraction elements
-// (128-byte row segments) per load, operand B (W, resident in L2) 32.  A ring: three slots
-// of [256 rows][64] (pipeline stage 2d + h is half h of A-stage d); B ring: four slots of
-// [256 rows][32].  A row of an A slot is 8 chunks of 16 B, chunk c of row r at position
-// c ^ xsw8(r): within 16 consecutive rows the pairs of rows that share a 256-byte bank
-// window take different chunks.
-constexpr int XA_BR = 2 * BR;                 // contraction elements per A stage
+// x-stage LDS: both operands move 64 contraction elements (128-byte row segments) per
+// load, into "double stages" (pipeline stage 2d + h is half h of double stage d).  A ring
+// (dg | dfc, streamed from HBM): three slots of [256 rows][64]; B ring (W, resident in L2):
+// two slots of [256 rows][64]; 160 KiB in all.  A row is 8 chunks of 16 B, chunk c of row r
+// at position c ^ xsw8(r): within 16 consecutive rows the pairs of rows that share a
+// 256-byte bank window take different chunks.
+constexpr int XA_BR = 2 * BR;                 // contraction elements per double stage
 constexpr int XA_SLOT = BP * XA_BR;           // elements per A slot (32 KiB)
-constexpr int XB_SLOT = BQ * BR;              // elements per B slot (16 KiB)
+constexpr int XB_SLOT = BQ * XA_BR;           // elements per B slot (32 KiB)
 constexpr int XA_LOADS = XA_SLOT * 2 / 1024 / (NT / 64);   // 1 KiB loads per wave: 8
-constexpr int XB_LOADS = XB_SLOT * 2 / 1024 / (NT / 64);   // 4
+constexpr int XB_LOADS = XB_SLOT * 2 / 1024 / (NT / 64);   // 8
 __device__ inline int xsw8(int r) { return (r >> 1) & 7; }
 
-// Fragments of one pipeline stage: half HALF of the A slot, and the B slot.
+// Fragments of one pipeline stage: half HALF of an A slot and of a B slot.
 template <typename T, int HALF>
 __device__ inline void x_read(const uint16_t* aslot, const uint16_t* bslot, int wp, int wq,
                               int lane, FragSet<T>& f) {
@@ -181,7 +181,7 @@ __device__ inline void x_read(const uint16_t* aslot, const uint16_t* bslot, int 
 #pragma unroll
     for (int j = 0; j < FQ; ++j) {
       const int r = wq * 128 + j * 32 + (lane & 31);
-      f.b[kk][j] = *reinterpret_cast<const F*>(bslot + r * BR + ((lc ^ xsw(r)) << 3));
+      f.b[kk][j] = *reinterpret_cast<const F*>(bslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
     }
   }
 }
@@ -415,20 +415,24 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
   } while (0)
 
 // ----------------------------------------------------------------- x stage (NT)
-// A = [dg | dfc] rows p (M), B = [W_g | W_fc] rows q (K).  Pipeline stage s < sN contracts
-// over columns 32 s .. of dg / W_g, stage s >= sN over the same columns of dfc / W_fc
-// (sN = 2 max(2, ceil(N / 64)), so that A stage d = s / 2 never straddles dg and dfc;
-// columns past N read zeros).  Tile L covers rows (L / nq) * 256 and columns (L % nq) * 256.
+// A = [dg | dfc] rows p (M), B = [W_g | W_fc] rows q (K).  Double stage d < sD contracts
+// over columns 64 d .. of dg / W_g, d >= sD over the same columns of dfc / W_fc
+// (sD = max(2, ceil(N / 64)); columns past N read zeros).  Tile L covers rows (L / nq) * 256
+// and columns (L % nq) * 256.
 //
-// Step t of a tile (stages run four steps deep in B and, at odd steps, two A stages deep):
-//   wait until this wave's loads of B stage t + 1 and of A stage (t + 1) / 2 landed and its
-//   own LDS reads are done; barrier; issue B stage t + 4 into the B slot just consumed; at
-//   odd t = 2d + 1 also issue A stage d + 3 into the A slot of A stage d (both of its halves
-//   were read by now); read stage t + 1 into the other register set while the MFMAs run on
-//   stage t.  Every wave issues 4 B loads per step and 8 A loads per odd step, so "the
-//   stages needed next have landed" is "at most 24 (even t) / 16 (odd t) loads outstanding";
-//   the prologue issues in the same order (A0 B0 B1 A1 B2 B3 A2).  Issues past the tile's
-//   last stage fetch the next tile's first stages (uniform selects, no branch).
+// Two steps per double stage d (stages t = 2d, 2d + 1):
+//   even t: read stage t + 1 (the second halves of the A and B slots of double stage d,
+//           which landed with the first) into the other register set while the MFMAs run
+//           on stage t; no wait, no barrier, no load;
+//   odd t:  wait until this wave's loads of double stage d + 1 landed and its own LDS
+//           reads are done; barrier (every wave's loads landed; every wave finished reading
+//           both slots of double stage d); issue B double stage d + 2 into the B slot and A
+//           double stage d + 3 into the A slot of double stage d; read stage t + 1 (first
+//           halves of double stage d + 1) while the MFMAs run on stage t.
+// Every wave issues 8 B then 8 A loads per odd step, so "double stage d + 1 landed" is "at
+// most 8 loads outstanding" (only A of d + 3 was issued after B of d + 1); the prologue
+// issues in the same order (A0 B0 A1 B1 A2).  Issues past the tile's last double stage
+// fetch the next tile's first ones (uniform selects, no branch).
 struct XTile {   // first row of the dg/dfc panel and of the W panel; 32-bit (M < 2^31)
   int p0, q0;
   bool live;
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const T* __restrict__ dg, const T* __restrict__ dfc, const T* __restrict__ wg,
     const T* __restrict__ wfc, T* __restrict__ dx, int64_t M, int64_t K, int64_t N, int64_t nq,
     int64_t ntiles) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[3 * XA_SLOT + 4 * XB_SLOT];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[3 * XA_SLOT + 2 * XB_SLOT];
   uint16_t* const ra0 = ring;
   uint16_t* const rb0 = ring + 3 * XA_SLOT;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -457,34 +461,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int64_t G = gridDim.x;
   const int64_t f0 = xcd_remap(blockIdx.x, G);
   const int64_t my_tiles = ntiles > f0 ? (ntiles - f0 + G - 1) / G : 0;
-  // A stages per dg (or dfc) half, at least 2 so that a tile has at least 4: the A loads
-  // run up to three A stages ahead and must stay within the next tile
+  // double stages per dg (or dfc) half, at least 2 so that a tile has at least 4: the A
+  // loads run up to three double stages ahead and must stay within the next tile
   int sD = (int)((N + XA_BR - 1) / XA_BR);
   if (sD < 2) sD = 2;
-  const int sN = 2 * sD;                           // pipeline stages per half
-  const int nst = 2 * sN;                          // pipeline stages per tile (multiple of 4)
-  const int nds = sN;                              // A stages per tile
+  const int nds = 2 * sD;                          // double stages per tile (even, >= 4)
+  const int nst = 2 * nds;                         // pipeline stages per tile (multiple of 4)
 
-  // A: a 1 KiB load covers 8 rows x 8 chunks, rows 64 wave + 8 i + lane / 8 (i = 0..7);
-  // B: 16 rows x 4 chunks, rows 64 wave + 16 i + lane / 4 (i = 0..3).  The lane fetches
-  // the logical chunk that its LDS position holds under the swizzle.
-  // The swizzles depend only on (lane, i parity) for A and on the lane for B:
-  // xsw8(64 wave + 8 i + lane / 8) = (4 i + lane / 16) % 8, xsw(64 wave + 16 i + lane / 4) =
-  // (lane / 16) % 4; so the column terms take two values (A) and one (B) per lane.
-  uint32_t aoff[8], boff[4];
+  // A and B alike: a 1 KiB load covers 8 rows x 8 chunks, rows 64 wave + 8 i + lane / 8
+  // (i = 0..7); the lane fetches the logical chunk that its LDS position holds under the
+  // swizzle.  xsw8(64 wave + 8 i + lane / 8) = (4 i + lane / 16) % 8, so the column term
+  // takes two values per lane; dg, dfc, W_g and W_fc all have rows of N elements, so the
+  // offsets serve both operands.
+  uint32_t aoff[8];
   int acol[2];
   acol[0] = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
   acol[1] = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
-  const int bcol = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = 64 * wave + 8 * i + (lane >> 3);
     aoff[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)acol[i & 1] * 2u;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 64 * wave + 16 * i + (lane >> 2);
-    boff[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)bcol * 2u;
   }
   // A stage d of tile c (d >= nds: stage d - nds of tile n) into an A slot
   auto issue_a = [&](const XTile& c, const XTile& n, int d, uint16_t* slot) {
@@ -515,86 +511,87 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     dma16<6 * 1024>(r, o[6], dst);
     dma16<7 * 1024>(r, o[7], dst);
   };
-  // B stage s of tile c (s >= nst: stage s - nst of tile n) into a B slot
-  auto issue_b = [&](const XTile& c, const XTile& n, int s, uint16_t* slot) {
-    asm volatile("" : "+s"(s));
-    const bool nx = s >= nst;
+  // B double stage d of tile c (d >= nds: double stage d - nds of tile n) into a B slot
+  auto issue_b = [&](const XTile& c, const XTile& n, int d, uint16_t* slot) {
+    asm volatile("" : "+s"(d));
+    const bool nx = d >= nds;
     const int q0 = __builtin_amdgcn_readfirstlane(nx ? n.q0 : c.q0);
     const bool live = __builtin_amdgcn_readfirstlane((nx ? n.live : c.live) ? 1 : 0) != 0;
-    const int ss = nx ? s - nst : s;
-    const bool hi = ss >= sN;
-    const int col0 = (hi ? ss - sN : ss) * BR;
+    const int dd = nx ? d - nds : d;
+    const bool hi = dd >= sD;
+    const int col0 = (hi ? dd - sD : dd) * XA_BR;
     const int rows = live ? ((int)K - q0 < BQ ? (int)K - q0 : BQ) : 0;
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc((hi ? wfc : wg) + (int64_t)q0 * N, (uint32_t)rows * (uint32_t)(N * 2));
-    const uint16_t* dst = slot + 64 * wave * BR;
-    uint32_t o[4];
+    const uint16_t* dst = slot + 64 * wave * XA_BR;
+    uint32_t o[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = col0 + bcol < (int)N ? boff[i] + (uint32_t)col0 * 2u : kOOB;
-    dma16<0 * 16 * BR * 2>(r, o[0], dst);
-    dma16<1 * 16 * BR * 2>(r, o[1], dst);
-    dma16<2 * 16 * BR * 2>(r, o[2], dst);
-    dma16<3 * 16 * BR * 2>(r, o[3], dst);
+    for (int i = 0; i < 8; ++i)
+      o[i] = col0 + acol[i & 1] < (int)N ? aoff[i] + (uint32_t)col0 * 2u : kOOB;
+    dma16<0 * 1024>(r, o[0], dst);
+    dma16<1 * 1024>(r, o[1], dst);
+    dma16<2 * 1024>(r, o[2], dst);
+    dma16<3 * 1024>(r, o[3], dst);
+    dma16<4 * 1024>(r, o[4], dst);
+    dma16<5 * 1024>(r, o[5], dst);
+    dma16<6 * 1024>(r, o[6], dst);
+    dma16<7 * 1024>(r, o[7], dst);
   };
 #define X_READ(h, as, bs, f) x_read<T, (h)>((as), (bs), wp, wq, lane, (f))
-  // one pipeline step u (= t mod 4) of a round starting at stage t0; `as` is the A slot of
-  // A stage t / 2; READ_NEXT = 0 on the last step of a tile
-#define X_STEP(u, READ_NEXT)                                                              \
+  // even step: second halves of the current double stage
+#define X_STEP_EVEN()                                                                     \
   do {                                                                                    \
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(((u) & 1) ? 2 * XB_LOADS + XA_LOADS                \
-                                                  : 2 * XB_LOADS + 2 * XA_LOADS));        \
+    X_READ(1, ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, frags[1]);                           \
+    stage_mma<T>(frags[0], acc);                                                          \
+    step_schedule<16>();                                                                  \
+  } while (0)
+  // odd step t = 2d + 1 (d = t0 / 2 + (u - 1) / 2); READ_NEXT = 0 on the last step of a tile
+#define X_STEP_ODD(d, READ_NEXT)                                                           \
+  do {                                                                                    \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(XA_LOADS));                                       \
     __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                                \
     SWG_COMPILER_FENCE();                                                                 \
     __builtin_amdgcn_s_barrier();                                                         \
     SWG_COMPILER_FENCE();                                                                 \
-    issue_b(cur, nxt, t0 + (u) + 4, rb0 + (u) * XB_SLOT);                                  \
-    if ((u) & 1) issue_a(cur, nxt, (t0 + (u)) / 2 + 3, ra0 + as * XA_SLOT);                \
-    if (READ_NEXT) {                                                                      \
-      if ((u) & 1) {                                                                      \
-        X_READ(0, ra0 + (as == 2 ? 0 : as + 1) * XA_SLOT, rb0 + (((u) + 1) & 3) * XB_SLOT,  \
-               frags[((u) + 1) & 1]);                                                     \
-      } else {                                                                            \
-        X_READ(1, ra0 + as * XA_SLOT, rb0 + (((u) + 1) & 3) * XB_SLOT, frags[((u) + 1) & 1]); \
-      }                                                                                   \
-    }                                                                                     \
-    stage_mma<T>(frags[(u) & 1], acc);                                                    \
+    issue_b(cur, nxt, (d) + 2, rb0 + bs * XB_SLOT);                                        \
+    issue_a(cur, nxt, (d) + 3, ra0 + as * XA_SLOT);                                        \
+    as = (as == 2 ? 0 : as + 1);                                                          \
+    bs ^= 1;                                                                              \
+    if (READ_NEXT) X_READ(0, ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, frags[0]);             \
+    stage_mma<T>(frags[1], acc);                                                          \
     if (READ_NEXT) step_schedule<16>();                                                   \
-    if ((u) & 1) as = (as == 2 ? 0 : as + 1);                                             \
   } while (0)
 
   f32x16 acc[FP][FQ];
   FragSet<T> frags[2];
   XTile cur = x_tile(f0, my_tiles > 0, nq);
   XTile nxt = x_tile(f0 + G, my_tiles > 1, nq);
-  int as = 0;   // A slot of the A stage holding the current pipeline stage
-  // prologue, in the steady-state issue order: A0 B0 B1 A1 B2 B3 A2
+  int as = 0, bs = 0;   // A and B slots of the double stage holding the current stage
+  // prologue, in the steady-state issue order: A0 B0 A1 B1 A2
   issue_a(cur, nxt, 0, ra0);
   issue_b(cur, nxt, 0, rb0);
-  issue_b(cur, nxt, 1, rb0 + XB_SLOT);
   issue_a(cur, nxt, 1, ra0 + XA_SLOT);
-  issue_b(cur, nxt, 2, rb0 + 2 * XB_SLOT);
-  issue_b(cur, nxt, 3, rb0 + 3 * XB_SLOT);
+  issue_b(cur, nxt, 1, rb0 + XB_SLOT);
   issue_a(cur, nxt, 2, ra0 + 2 * XA_SLOT);
-  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * XB_LOADS + 2 * XA_LOADS));   // A0 and B0 landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * XA_LOADS + XB_LOADS));   // A0 and B0 landed
   SWG_COMPILER_FENCE();
   __builtin_amdgcn_s_barrier();
   SWG_COMPILER_FENCE();
   for (int64_t j = 0; j < my_tiles; ++j) {
     nxt = x_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
     zero_acc(acc);
-    X_READ(0, ra0 + as * XA_SLOT, rb0, frags[0]);   // stage 0 (A half 0, B slot 0)
-    int t0 = 0;
-    for (; t0 + 4 < nst; t0 += 4) {
-      X_STEP(0, 1);
-      X_STEP(1, 1);
-      X_STEP(2, 1);
-      X_STEP(3, 1);
+    X_READ(0, ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, frags[0]);   // stage 0
+    int d0 = 0;
+    for (; d0 + 2 < nds; d0 += 2) {
+      X_STEP_EVEN();
+      X_STEP_ODD(d0, 1);
+      X_STEP_EVEN();
+      X_STEP_ODD(d0 + 1, 1);
     }
-    X_STEP(0, 1);
-    X_STEP(1, 1);
-    X_STEP(2, 1);
-    X_STEP(3, 0);
+    X_STEP_EVEN();
+    X_STEP_ODD(d0, 1);
+    X_STEP_EVEN();
+    X_STEP_ODD(d0 + 1, 0);
     // epilogue: straight from the accumulators, two adjacent columns per 32-bit store
     {
       const int rows = (int)M - cur.p0 < BP ? (int)M - cur.p0 : BP;
@@ -604,7 +601,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
     cur = nxt;
   }
-#undef X_STEP
+#undef X_STEP_EVEN
+#undef X_STEP_ODD
 #undef X_READ
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
