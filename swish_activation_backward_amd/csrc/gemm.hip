@@ -9,22 +9,25 @@
 // 256 fp32 accumulators live in the AGPR file.
 //
 // Operands move global -> LDS with buffer_load ... lds (the load unit writes LDS
-// directly; no registers, no ds_write).  LDS is a ring of four 32-deep contraction
-// stages (32 KiB each), and operand fragments are double-buffered in registers: while the
-// matrix cores multiply stage t from registers, the fragments of stage t+1 are read from
-// LDS and stages t+2..t+4 are in flight.  A stage is read only after `s_waitcnt vmcnt`
-// says this wave's part of it landed and a barrier says every wave's part did.  Rows and columns outside the
+// directly; no registers, no ds_write), and operand fragments are double-buffered in
+// registers: while the matrix cores multiply one 32-deep stage from registers, the
+// fragments of the next stage are read from LDS and later stages are in flight.  A stage
+// is read only after `s_waitcnt vmcnt` says this wave's part of it landed and a barrier
+// says every wave's part did.  The loads of a step and the next stage's LDS reads are
+// spread between that step's MFMAs (scheduling fences fix the order), so the load issue
+// does not stall the matrix cores behind the barrier.  Rows and columns outside the
 // tensors (ragged M, partial tiles, stages past the end) are fetched at offsets beyond
 // the buffer window and arrive as zeros from the hardware range check: the loop has no
 // data-path branches.
 //
-//   x stage: both operands are contraction-contiguous in memory; LDS keeps them as
-//            [row][32 contraction] and each lane reads one MFMA operand (8 consecutive
-//            contraction elements) with a 16-byte ds_read_b128.
+//   x stage: both operands are contraction-contiguous in memory; LDS holds three 64-deep
+//            slots of [dg | dfc] rows and two of [W_g | W_fc] rows, [row][64] each, and
+//            each lane reads one MFMA operand (8 consecutive contraction elements) with
+//            a 16-byte ds_read_b128.
 //   w stage: both operands are contraction-strided (the contraction runs over the rows
-//            of x and dg); LDS keeps them as loaded, [32 contraction][256 columns], and
-//            the operands are read with the gfx950 transposing LDS read
-//            ds_read_b64_tr_b16 (two per operand).
+//            of x and dg); LDS is a ring of four 32-deep stages kept as loaded,
+//            [32 contraction][256 columns] per operand, and the operands are read with
+//            the gfx950 transposing LDS read ds_read_b64_tr_b16 (two per operand).
 // Every LDS tile is XOR-swizzled in 16-byte chunks (the swizzle is applied to the
 // global address each lane fetches, since the LDS write order is fixed by the load
 // unit) so that the operand reads of one instruction hit distinct banks.
@@ -39,6 +42,8 @@
 // accumulators).  Work is dealt so that concurrently running tiles with neighbouring
 // indices sit on one XCD (the hardware deals workgroup ids round-robin over the 8
 // XCDs): tiles sharing an operand panel then share that XCD's L2.
+#include <utility>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -426,13 +431,20 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
 //           on stage t; no wait, no barrier, no load;
 //   odd t:  wait until this wave's loads of double stage d + 1 landed and its own LDS
 //           reads are done; barrier (every wave's loads landed; every wave finished reading
-//           both slots of double stage d); issue B double stage d + 2 into the B slot and A
-//           double stage d + 3 into the A slot of double stage d; read stage t + 1 (first
-//           halves of double stage d + 1) while the MFMAs run on stage t.
+//           both slots of double stage d); then, spread between the MFMAs of stage t, issue
+//           B double stage d + 2 into the B slot and A double stage d + 3 into the A slot of
+//           double stage d, and read stage t + 1 (first halves of double stage d + 1).
 // Every wave issues 8 B then 8 A loads per odd step, so "double stage d + 1 landed" is "at
 // most 8 loads outstanding" (only A of d + 3 was issued after B of d + 1); the prologue
 // issues in the same order (A0 B0 A1 B1 A2).  Issues past the tile's last double stage
 // fetch the next tile's first ones (uniform selects, no branch).
+//
+// Issue cost: a load's address is window base + soffset + voffset.  The window (the
+// operand panel of a tile, dg or dfc half) is formed once per tile; the column of the
+// double stage goes into the scalar soffset; the per-lane voffset (row and swizzled chunk)
+// is fixed.  The hardware range check applies to voffset only, against the window's rows,
+// so rows past the end still read zeros.  Only when N is not a multiple of 64 does the
+// last double stage of each half need a per-lane column test (template RAGGED).
 struct XTile {   // first row of the dg/dfc panel and of the W panel; 32-bit (M < 2^31)
   int p0, q0;
   bool live;
@@ -447,7 +459,142 @@ __device__ inline XTile x_tile(int64_t L, bool live, int64_t nq) {
   return c;
 }
 
+// 64-bit pointer pinned to scalar registers (a buffer resource must be wave-uniform)
+template <typename P>
+__device__ inline P* uniform_ptr(P* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (P*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Operand windows of one tile: the dg and dfc row panels and the W_g and W_fc row panels,
+// each with its valid byte count (0 for a tile that does not exist: every load reads 0).
+struct XWin {
+  int64_t a_off, b_off;        // element offsets of the panels (p0 N, q0 N)
+  uint32_t a_bytes, b_bytes;
+};
+
+__device__ inline XWin x_win(const XTile& c, int64_t M, int64_t K, int64_t N) {
+  XWin w;
+  const int64_t ra = c.live ? (M - c.p0 < BP ? M - c.p0 : BP) : 0;
+  const int64_t rb = c.live ? (K - c.q0 < BQ ? K - c.q0 : BQ) : 0;
+  w.a_off = (int64_t)c.p0 * N;
+  w.b_off = (int64_t)c.q0 * N;
+  w.a_bytes = (uint32_t)(ra * N * 2);
+  w.b_bytes = (uint32_t)(rb * N * 2);
+  return w;
+}
+
+// One issue: window, soffset (column of the double stage, bytes) and LDS destination.
+struct XIssue {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t soff;
+  int lim;                 // columns left in the half from this double stage on
+  const uint16_t* dst;
+};
+
+// Double stage d of operand A (IS_A) or B of the current tile (d >= nds: double stage
+// d - nds of the next tile).
 template <typename T>
+__device__ inline XIssue x_issue(const T* lo, const T* hi_arr, XWin wc, XWin wn, bool is_a, int d,
+                                 int nds, int sD, int64_t N, uint16_t* slot) {
+  const bool nx = d >= nds;
+  const int dd = nx ? d - nds : d;
+  const bool hi = dd >= sD;
+  const int col = (hi ? dd - sD : dd) * XA_BR;
+  const int64_t off = is_a ? (nx ? wn.a_off : wc.a_off) : (nx ? wn.b_off : wc.b_off);
+  const uint32_t bytes = is_a ? (nx ? wn.a_bytes : wc.a_bytes) : (nx ? wn.b_bytes : wc.b_bytes);
+  XIssue is;
+  is.r = make_rsrc(uniform_ptr((hi ? hi_arr : lo) + off), __builtin_amdgcn_readfirstlane(bytes));
+  is.soff = __builtin_amdgcn_readfirstlane((uint32_t)col * 2u);
+  is.lim = (int)N - col;
+  is.dst = slot;
+  return is;
+}
+
+// This lane's voffset for load i (0..7) of an issue.
+template <bool RAGGED>
+__device__ inline uint32_t x_voff(const XIssue& is, const uint32_t (&aoff)[8], const int (&acol)[2],
+                                  int i) {
+  if (!RAGGED) return aoff[i];
+  return acol[i & 1] < is.lim ? aoff[i] : kOOB;
+}
+
+// dma16 with a wave-uniform byte offset in soffset (not range-checked: the window's rows
+// are checked through voffset alone)
+template <int OFS>
+__device__ inline void dma16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                              const uint16_t* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(LDS_AS const void*)dst);
+  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, %4 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds), "i"(OFS), "s"(soff)
+               : "memory", "scc");
+}
+
+template <bool RAGGED>
+__device__ inline void x_issue_all(const XIssue& is, const uint32_t (&aoff)[8],
+                                   const int (&acol)[2]) {
+  dma16s<0 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 0), is.soff, is.dst);
+  dma16s<1 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 1), is.soff, is.dst);
+  dma16s<2 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 2), is.soff, is.dst);
+  dma16s<3 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 3), is.soff, is.dst);
+  dma16s<4 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 4), is.soff, is.dst);
+  dma16s<5 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 5), is.soff, is.dst);
+  dma16s<6 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 6), is.soff, is.dst);
+  dma16s<7 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 7), is.soff, is.dst);
+}
+
+// Fragment G (0..15, in x_read's order: kk = G / 8; G % 8 < 4: A block G % 4, else B
+// block G % 4) of stage half HALF.
+template <typename T, int HALF, int G>
+__device__ inline void x_read_one(const uint16_t* aslot, const uint16_t* bslot, int wp, int wq,
+                                  int lane, FragSet<T>& f) {
+  using F = typename Mfma<T>::frag;
+  constexpr int kk = G / 8, blk = G % 4;
+  const int lc = 2 * kk + (lane >> 5);
+  if (G % 8 < 4) {
+    const int r = wp * 128 + blk * 32 + (lane & 31);
+    f.a[kk][blk] = *reinterpret_cast<const F*>(aslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
+  } else {
+    const int r = wq * 128 + blk * 32 + (lane & 31);
+    f.b[kk][blk] = *reinterpret_cast<const F*>(bslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
+  }
+}
+
+// Group G of an odd step: MFMAs 2G, 2G + 1 of the stage in f (stage_mma's order), fragment
+// G of the next stage (READ_NEXT), and load G % 8 of the B issue (G < 8) or of the A issue.
+// The scheduling fence keeps the groups in this order, so that the 16 loads and the
+// address work around them are spread over the step instead of stalling the matrix cores
+// behind the barrier.
+template <typename T, bool RAGGED, bool READ_NEXT, int G>
+__device__ inline void x_odd_group(f32x16 (&acc)[FP][FQ], const FragSet<T>& f, FragSet<T>& fn,
+                                   const uint16_t* aslot, const uint16_t* bslot, int wp, int wq,
+                                   int lane, const XIssue& is, const uint32_t (&aoff)[8],
+                                   const int (&acol)[2]) {
+  constexpr int kk = G >> 3, i = (G >> 1) & 3, j = (G & 1) * 2;
+  acc[i][j] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j], acc[i][j]);
+  acc[i][j + 1] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j + 1], acc[i][j + 1]);
+  if (READ_NEXT) x_read_one<T, 0, G>(aslot, bslot, wp, wq, lane, fn);
+  dma16s<(G & 7) * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, G & 7), is.soff, is.dst);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename T, bool RAGGED, bool READ_NEXT, int... G>
+__device__ inline void x_odd_groups(std::integer_sequence<int, G...>, f32x16 (&acc)[FP][FQ],
+                                    const FragSet<T>& f, FragSet<T>& fn, const uint16_t* aslot,
+                                    const uint16_t* bslot, int wp, int wq, int lane,
+                                    const XIssue& is, const uint32_t (&aoff)[8],
+                                    const int (&acol)[2]) {
+  (x_odd_group<T, RAGGED, READ_NEXT, G>(acc, f, fn, aslot, bslot, wp, wq, lane, is, aoff, acol),
+   ...);
+}
+using XGroupsB = std::integer_sequence<int, 0, 1, 2, 3, 4, 5, 6, 7>;
+using XGroupsA = std::integer_sequence<int, 8, 9, 10, 11, 12, 13, 14, 15>;
+
+template <typename T, bool RAGGED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void x_stage_kernel(
     const T* __restrict__ dg, const T* __restrict__ dfc, const T* __restrict__ wg,
     const T* __restrict__ wfc, T* __restrict__ dx, int64_t M, int64_t K, int64_t N, int64_t nq,
@@ -466,7 +613,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   int sD = (int)((N + XA_BR - 1) / XA_BR);
   if (sD < 2) sD = 2;
   const int nds = 2 * sD;                          // double stages per tile (even, >= 4)
-  const int nst = 2 * nds;                         // pipeline stages per tile (multiple of 4)
 
   // A and B alike: a 1 KiB load covers 8 rows x 8 chunks, rows 64 wave + 8 i + lane / 8
   // (i = 0..7); the lane fetches the logical chunk that its LDS position holds under the
@@ -482,60 +628,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int row = 64 * wave + 8 * i + (lane >> 3);
     aoff[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)acol[i & 1] * 2u;
   }
-  // A stage d of tile c (d >= nds: stage d - nds of tile n) into an A slot
-  auto issue_a = [&](const XTile& c, const XTile& n, int d, uint16_t* slot) {
-    asm volatile("" : "+s"(d));   // keep per-stage offsets from being hoisted (they would
+  const int wofs = 64 * wave * XA_BR;   // this wave's rows in a slot
+  auto issue_a = [&](XWin wc, XWin wn, int d, uint16_t* slot) {
+    asm volatile("" : "+s"(d));   // keep per-stage values from being hoisted (they would
                                   // stay live across the tile loop, and spill)
-    const bool nx = d >= nds;
-    // value selects (no branch in the pipeline), pinned to scalar registers: the buffer
-    // window must be wave-uniform
-    const int p0 = __builtin_amdgcn_readfirstlane(nx ? n.p0 : c.p0);
-    const bool live = __builtin_amdgcn_readfirstlane((nx ? n.live : c.live) ? 1 : 0) != 0;
-    const int dd = nx ? d - nds : d;
-    const bool hi = dd >= sD;
-    const int col0 = (hi ? dd - sD : dd) * XA_BR;
-    const int rows = live ? ((int)M - p0 < BP ? (int)M - p0 : BP) : 0;
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc((hi ? dfc : dg) + (int64_t)p0 * N, (uint32_t)rows * (uint32_t)(N * 2));
-    const uint16_t* dst = slot + 64 * wave * XA_BR;
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      o[i] = col0 + acol[i & 1] < (int)N ? aoff[i] + (uint32_t)col0 * 2u : kOOB;
-    dma16<0 * 1024>(r, o[0], dst);
-    dma16<1 * 1024>(r, o[1], dst);
-    dma16<2 * 1024>(r, o[2], dst);
-    dma16<3 * 1024>(r, o[3], dst);
-    dma16<4 * 1024>(r, o[4], dst);
-    dma16<5 * 1024>(r, o[5], dst);
-    dma16<6 * 1024>(r, o[6], dst);
-    dma16<7 * 1024>(r, o[7], dst);
+    return x_issue<T>(dg, dfc, wc, wn, true, d, nds, sD, N, slot + wofs);
   };
-  // B double stage d of tile c (d >= nds: double stage d - nds of tile n) into a B slot
-  auto issue_b = [&](const XTile& c, const XTile& n, int d, uint16_t* slot) {
+  auto issue_b = [&](XWin wc, XWin wn, int d, uint16_t* slot) {
     asm volatile("" : "+s"(d));
-    const bool nx = d >= nds;
-    const int q0 = __builtin_amdgcn_readfirstlane(nx ? n.q0 : c.q0);
-    const bool live = __builtin_amdgcn_readfirstlane((nx ? n.live : c.live) ? 1 : 0) != 0;
-    const int dd = nx ? d - nds : d;
-    const bool hi = dd >= sD;
-    const int col0 = (hi ? dd - sD : dd) * XA_BR;
-    const int rows = live ? ((int)K - q0 < BQ ? (int)K - q0 : BQ) : 0;
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc((hi ? wfc : wg) + (int64_t)q0 * N, (uint32_t)rows * (uint32_t)(N * 2));
-    const uint16_t* dst = slot + 64 * wave * XA_BR;
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      o[i] = col0 + acol[i & 1] < (int)N ? aoff[i] + (uint32_t)col0 * 2u : kOOB;
-    dma16<0 * 1024>(r, o[0], dst);
-    dma16<1 * 1024>(r, o[1], dst);
-    dma16<2 * 1024>(r, o[2], dst);
-    dma16<3 * 1024>(r, o[3], dst);
-    dma16<4 * 1024>(r, o[4], dst);
-    dma16<5 * 1024>(r, o[5], dst);
-    dma16<6 * 1024>(r, o[6], dst);
-    dma16<7 * 1024>(r, o[7], dst);
+    return x_issue<T>(wg, wfc, wc, wn, false, d, nds, sD, N, slot + wofs);
   };
 #define X_READ(h, as, bs, f) x_read<T, (h)>((as), (bs), wp, wq, lane, (f))
   // even step: second halves of the current double stage
@@ -553,45 +654,56 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     SWG_COMPILER_FENCE();                                                                 \
     __builtin_amdgcn_s_barrier();                                                         \
     SWG_COMPILER_FENCE();                                                                 \
-    issue_b(cur, nxt, (d) + 2, rb0 + bs * XB_SLOT);                                        \
-    issue_a(cur, nxt, (d) + 3, ra0 + as * XA_SLOT);                                        \
+    uint16_t* const bfree_ = rb0 + bs * XB_SLOT;                                          \
+    uint16_t* const afree_ = ra0 + as * XA_SLOT;                                          \
     as = (as == 2 ? 0 : as + 1);                                                          \
     bs ^= 1;                                                                              \
-    if (READ_NEXT) X_READ(0, ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, frags[0]);             \
-    stage_mma<T>(frags[1], acc);                                                          \
-    if (READ_NEXT) step_schedule<16>();                                                   \
+    const XIssue ib_ = issue_b(wc, wn, (d) + 2, bfree_);                                   \
+    x_odd_groups<T, RAGGED, (READ_NEXT)>(XGroupsB{}, acc, frags[1], frags[0],              \
+                                         ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, wp, wq,   \
+                                         lane, ib_, aoff, acol);                          \
+    const XIssue ia_ = issue_a(wc, wn, (d) + 3, afree_);                                   \
+    x_odd_groups<T, RAGGED, (READ_NEXT)>(XGroupsA{}, acc, frags[1], frags[0],              \
+                                         ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, wp, wq,   \
+                                         lane, ia_, aoff, acol);                          \
   } while (0)
 
   f32x16 acc[FP][FQ];
   FragSet<T> frags[2];
-  XTile cur = x_tile(f0, my_tiles > 0, nq);
   XTile nxt = x_tile(f0 + G, my_tiles > 1, nq);
+  XWin wc = x_win(x_tile(f0, my_tiles > 0, nq), M, K, N);
+  XWin wn = x_win(nxt, M, K, N);
   int as = 0, bs = 0;   // A and B slots of the double stage holding the current stage
   // prologue, in the steady-state issue order: A0 B0 A1 B1 A2
-  issue_a(cur, nxt, 0, ra0);
-  issue_b(cur, nxt, 0, rb0);
-  issue_a(cur, nxt, 1, ra0 + XA_SLOT);
-  issue_b(cur, nxt, 1, rb0 + XB_SLOT);
-  issue_a(cur, nxt, 2, ra0 + 2 * XA_SLOT);
+  x_issue_all<RAGGED>(issue_a(wc, wn, 0, ra0), aoff, acol);
+  x_issue_all<RAGGED>(issue_b(wc, wn, 0, rb0), aoff, acol);
+  x_issue_all<RAGGED>(issue_a(wc, wn, 1, ra0 + XA_SLOT), aoff, acol);
+  x_issue_all<RAGGED>(issue_b(wc, wn, 1, rb0 + XB_SLOT), aoff, acol);
+  x_issue_all<RAGGED>(issue_a(wc, wn, 2, ra0 + 2 * XA_SLOT), aoff, acol);
   __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * XA_LOADS + XB_LOADS));   // A0 and B0 landed
   SWG_COMPILER_FENCE();
   __builtin_amdgcn_s_barrier();
   SWG_COMPILER_FENCE();
   for (int64_t j = 0; j < my_tiles; ++j) {
-    nxt = x_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
+    const XTile cur = x_tile(f0 + j * G, true, nq);
+    if (j > 0) {
+      nxt = x_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
+      wc = wn;
+      wn = x_win(nxt, M, K, N);
+    }
     zero_acc(acc);
     X_READ(0, ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, frags[0]);   // stage 0
     int d0 = 0;
     for (; d0 + 2 < nds; d0 += 2) {
       X_STEP_EVEN();
-      X_STEP_ODD(d0, 1);
+      X_STEP_ODD(d0, true);
       X_STEP_EVEN();
-      X_STEP_ODD(d0 + 1, 1);
+      X_STEP_ODD(d0 + 1, true);
     }
     X_STEP_EVEN();
-    X_STEP_ODD(d0, 1);
+    X_STEP_ODD(d0, true);
     X_STEP_EVEN();
-    X_STEP_ODD(d0 + 1, 0);
+    X_STEP_ODD(d0 + 1, false);
     // epilogue: straight from the accumulators, two adjacent columns per 32-bit store
     {
       const int rows = (int)M - cur.p0 < BP ? (int)M - cur.p0 : BP;
@@ -599,7 +711,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                          make_rsrc(dx + (int64_t)cur.p0 * K + cur.q0, clamp_bytes(rows, K * 2)),
                          (uint32_t)(K * 2), wp * 128, wq * 128, (int)K - cur.q0);
     }
-    cur = nxt;
   }
 #undef X_STEP_EVEN
 #undef X_STEP_ODD
@@ -633,7 +744,79 @@ __device__ inline WItem w_item(int64_t L, bool live, int64_t tiles, int64_t tnh,
   return w;
 }
 
-template <typename T>
+// One w-stage issue: the stage's row windows of x and of dg (or dfc), the tile's first
+// columns as scalar soffsets (bytes) and the columns left in the tile (ragged edges only).
+struct WIssue {
+  __amdgpu_buffer_rsrc_t rx, rd;
+  uint32_t sx, sd;
+  int kleft, nleft;
+  const uint16_t* dst;
+};
+
+// Load e (0..7) of a w-stage issue: e < 4 fetches rows of x, e >= 4 rows of dg / dfc.
+template <bool RAGGED, int E>
+__device__ inline void w_dma(const WIssue& is, const uint32_t (&xbase)[4],
+                             const uint32_t (&dbase)[4], const int (&lcol)[4]) {
+  constexpr int i = E & 3;
+  if (E < 4) {
+    const uint32_t v = !RAGGED || lcol[i] < is.kleft ? xbase[i] : kOOB;
+    dma16s<i * 2 * BP * 2>(is.rx, v, is.sx, is.dst);
+  } else {
+    const uint32_t v = !RAGGED || lcol[i] < is.nleft ? dbase[i] : kOOB;
+    dma16s<BR * BP * 2 + i * 2 * BP * 2>(is.rd, v, is.sd, is.dst);
+  }
+}
+
+template <bool RAGGED>
+__device__ inline void w_issue_all(const WIssue& is, const uint32_t (&xbase)[4],
+                                   const uint32_t (&dbase)[4], const int (&lcol)[4]) {
+  w_dma<RAGGED, 0>(is, xbase, dbase, lcol);
+  w_dma<RAGGED, 1>(is, xbase, dbase, lcol);
+  w_dma<RAGGED, 2>(is, xbase, dbase, lcol);
+  w_dma<RAGGED, 3>(is, xbase, dbase, lcol);
+  w_dma<RAGGED, 4>(is, xbase, dbase, lcol);
+  w_dma<RAGGED, 5>(is, xbase, dbase, lcol);
+  w_dma<RAGGED, 6>(is, xbase, dbase, lcol);
+  w_dma<RAGGED, 7>(is, xbase, dbase, lcol);
+}
+
+// Fragment G (0..15, w_read's order) of a w-stage slot.
+template <typename T, int G>
+__device__ inline void w_read_one(const uint16_t* slot, const int (&aoff)[FP],
+                                  const int (&boff)[FQ], FragSet<T>& f) {
+  constexpr int ks = G / 8, blk = G % 4;
+  if (G % 8 < 4) f.a[ks][blk] = w_frag<T>(slot + 16 * ks * BQ + aoff[blk]);
+  else f.b[ks][blk] = w_frag<T>(slot + BR * BP + 16 * ks * BQ + boff[blk]);
+}
+
+// Group G of a w step: MFMAs 2G, 2G + 1 of the stage in f, fragment G of the next stage
+// (READ_NEXT) and, in odd groups, load G / 2 of the issue, kept in this order by the
+// scheduling fence (see x_odd_group).
+template <typename T, bool RAGGED, bool READ_NEXT, int G>
+__device__ inline void w_group(f32x16 (&acc)[FP][FQ], const FragSet<T>& f, FragSet<T>& fn,
+                               const uint16_t* next_slot, const int (&aoff)[FP],
+                               const int (&boff)[FQ], const WIssue& is,
+                               const uint32_t (&xbase)[4], const uint32_t (&dbase)[4],
+                               const int (&lcol)[4]) {
+  constexpr int kk = G >> 3, i = (G >> 1) & 3, j = (G & 1) * 2;
+  acc[i][j] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j], acc[i][j]);
+  acc[i][j + 1] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j + 1], acc[i][j + 1]);
+  if (READ_NEXT) w_read_one<T, G>(next_slot, aoff, boff, fn);
+  if (G & 1) w_dma<RAGGED, (G >> 1)>(is, xbase, dbase, lcol);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename T, bool RAGGED, bool READ_NEXT, int... G>
+__device__ inline void w_groups(std::integer_sequence<int, G...>, f32x16 (&acc)[FP][FQ],
+                                const FragSet<T>& f, FragSet<T>& fn, const uint16_t* next_slot,
+                                const int (&aoff)[FP], const int (&boff)[FQ], const WIssue& is,
+                                const uint32_t (&xbase)[4], const uint32_t (&dbase)[4],
+                                const int (&lcol)[4]) {
+  (w_group<T, RAGGED, READ_NEXT, G>(acc, f, fn, next_slot, aoff, boff, is, xbase, dbase, lcol),
+   ...);
+}
+
+template <typename T, bool RAGGED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void w_stage_kernel(
     const T* __restrict__ x, const T* __restrict__ dg, const T* __restrict__ dfc,
     T* __restrict__ dwg, T* __restrict__ dwfc, float* __restrict__ ws, int64_t M, int64_t K,
@@ -665,19 +848,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int rows = w.live ? ((w.m_end - m0 < BR) ? w.m_end - m0 : BR) : 0;
     const int64_t mb = rows > 0 ? m0 : 0;
     const T* d = w.hi ? dfc : dg;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + mb * K, clamp_bytes(rows, K * 2));
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(d + mb * N, clamp_bytes(rows, N * 2));
-    const int kleft = (int)K - w.k0, nleft = (int)N - w.n0;   // columns left in the tile
-    const uint32_t k2 = (uint32_t)w.k0 * 2u, n2 = (uint32_t)w.n0 * 2u;
-    const uint16_t* dst = slot + 8 * wave * BP;   // this wave's 4 row pairs
-    dma16<0 * 2 * BP * 2>(rx, lcol[0] < kleft ? xbase[0] + k2 : kOOB, dst);
-    dma16<1 * 2 * BP * 2>(rx, lcol[1] < kleft ? xbase[1] + k2 : kOOB, dst);
-    dma16<2 * 2 * BP * 2>(rx, lcol[2] < kleft ? xbase[2] + k2 : kOOB, dst);
-    dma16<3 * 2 * BP * 2>(rx, lcol[3] < kleft ? xbase[3] + k2 : kOOB, dst);
-    dma16<BR * BP * 2 + 0 * 2 * BP * 2>(rd, lcol[0] < nleft ? dbase[0] + n2 : kOOB, dst);
-    dma16<BR * BP * 2 + 1 * 2 * BP * 2>(rd, lcol[1] < nleft ? dbase[1] + n2 : kOOB, dst);
-    dma16<BR * BP * 2 + 2 * 2 * BP * 2>(rd, lcol[2] < nleft ? dbase[2] + n2 : kOOB, dst);
-    dma16<BR * BP * 2 + 3 * 2 * BP * 2>(rd, lcol[3] < nleft ? dbase[3] + n2 : kOOB, dst);
+    WIssue is;
+    is.rx = make_rsrc(uniform_ptr(x + mb * K), __builtin_amdgcn_readfirstlane(clamp_bytes(rows, K * 2)));
+    is.rd = make_rsrc(uniform_ptr(d + mb * N), __builtin_amdgcn_readfirstlane(clamp_bytes(rows, N * 2)));
+    is.sx = __builtin_amdgcn_readfirstlane((uint32_t)w.k0 * 2u);
+    is.sd = __builtin_amdgcn_readfirstlane((uint32_t)w.n0 * 2u);
+    is.kleft = (int)K - w.k0;   // columns left in the tile
+    is.nleft = (int)N - w.n0;
+    is.dst = slot + 8 * wave * BP;   // this wave's 4 row pairs
+    return is;
   };
 
   int aoff[FP], boff[FQ];
@@ -687,19 +866,51 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     boff[i] = aoff[i] + wq * 128;
     aoff[i] += wp * 128;
   }
-#define W_ISSUE(c, s, slot) issue((c), (s), (slot))
 #define W_READ(slot, f) w_read<T>((slot), aoff, boff, (f))
-  constexpr int READS_PER_STEP = 32;   // ds_read_b64_tr_b16: 2 per fragment
+  // one pipeline step u (0..3): as SWG_PIPE_STEP, with the stage's loads and the next
+  // stage's fragment reads spread between the MFMAs
+#define W_STEP(ctx, st, u, READ_NEXT)                                                       \
+  do {                                                                                    \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));                            \
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                                \
+    SWG_COMPILER_FENCE();                                                                 \
+    __builtin_amdgcn_s_barrier();                                                         \
+    SWG_COMPILER_FENCE();                                                                 \
+    const WIssue is_ = issue((ctx), (st), ring + (u) * SLOT);                              \
+    w_groups<T, RAGGED, (READ_NEXT)>(std::make_integer_sequence<int, 16>{}, acc,           \
+                                     frags[(u) & 1], frags[((u) + 1) & 1],                \
+                                     ring + (((u) + 1) & 3) * SLOT, aoff, boff, is_, xbase, \
+                                     dbase, lcol);                                        \
+  } while (0)
 
   f32x16 acc[FP][FQ];
   FragSet<T> frags[2];
   WItem cur = w_item(f0, my_items > 0, tiles, tnh, split_rows, M);
-  SWG_PIPE_PROLOGUE(W_ISSUE, cur);
+  // prologue: the first four stages in flight, the first landed for every wave
+  w_issue_all<RAGGED>(issue(cur, 0, ring), xbase, dbase, lcol);
+  w_issue_all<RAGGED>(issue(cur, 1, ring + SLOT), xbase, dbase, lcol);
+  w_issue_all<RAGGED>(issue(cur, 2, ring + 2 * SLOT), xbase, dbase, lcol);
+  w_issue_all<RAGGED>(issue(cur, 3, ring + 3 * SLOT), xbase, dbase, lcol);
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * LOADS_PER_STAGE));
+  SWG_COMPILER_FENCE();
+  __builtin_amdgcn_s_barrier();
+  SWG_COMPILER_FENCE();
   const int64_t R2 = 2 * N;
   for (int64_t j = 0; j < my_items; ++j) {
     const WItem nxt = w_item(f0 + (j + 1) * G, j + 1 < my_items, tiles, tnh, split_rows, M);
     zero_acc(acc);
-    SWG_TILE_ROUNDS(W_ISSUE, W_READ, frags, cur, nxt, cur.nst);
+    W_READ(ring, frags[0]);
+    int64_t t = 0;
+    for (; t + 4 < cur.nst; t += 4) {
+      W_STEP(cur, t + 4, 0, true);
+      W_STEP(cur, t + 5, 1, true);
+      W_STEP(cur, t + 6, 2, true);
+      W_STEP(cur, t + 7, 3, true);
+    }
+    W_STEP(nxt, 0, 0, true);
+    W_STEP(nxt, 1, 1, true);
+    W_STEP(nxt, 2, 2, true);
+    W_STEP(nxt, 3, 3, false);   // the next tile's first stage is read after the epilogue
     // epilogue: rows k, columns n (of dg or dfc) straight from the accumulators
     const int64_t k0 = (int64_t)cur.k0 + wp * 128, n0 = (int64_t)cur.n0 + wq * 128;
     if (ws != nullptr) {
@@ -722,7 +933,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
     cur = nxt;
   }
-#undef W_ISSUE
+#undef W_STEP
 #undef W_READ
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
@@ -957,10 +1168,16 @@ static hipError_t x_stage_t(const void* dg, const void* dfc, const void* wg, con
   const int64_t np = ceil_div(M, BP), nq = ceil_div(K, BQ);
   const int64_t ntiles = np * nq;
   const int64_t grid = ntiles < cus ? ntiles : cus;
-  hipLaunchKernelGGL((x_stage_kernel<T>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                     static_cast<const T*>(dg), static_cast<const T*>(dfc),
-                     static_cast<const T*>(wg), static_cast<const T*>(wfc), static_cast<T*>(dx),
-                     M, K, N, nq, ntiles);
+  if (N % XA_BR == 0)
+    hipLaunchKernelGGL((x_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       static_cast<const T*>(dg), static_cast<const T*>(dfc),
+                       static_cast<const T*>(wg), static_cast<const T*>(wfc),
+                       static_cast<T*>(dx), M, K, N, nq, ntiles);
+  else
+    hipLaunchKernelGGL((x_stage_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       static_cast<const T*>(dg), static_cast<const T*>(dfc),
+                       static_cast<const T*>(wg), static_cast<const T*>(wfc),
+                       static_cast<T*>(dx), M, K, N, nq, ntiles);
   return hipGetLastError();
 }
 
@@ -978,10 +1195,16 @@ static hipError_t w_stage_t(const WPlan& p, const void* x, const void* dg, const
   float* wsp = p.splits > 1 ? ws : nullptr;
   const int64_t nitems = p.splits * p.tiles;
   const int64_t grid = nitems < cus ? nitems : cus;
-  hipLaunchKernelGGL((w_stage_kernel<T>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                     static_cast<const T*>(x), static_cast<const T*>(dg),
-                     static_cast<const T*>(dfc), static_cast<T*>(dwg), static_cast<T*>(dwfc), wsp,
-                     M, K, N, p.tn / 2, p.tiles, p.rows, nitems);
+  if (K % BP == 0 && N % BQ == 0)
+    hipLaunchKernelGGL((w_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       static_cast<const T*>(x), static_cast<const T*>(dg),
+                       static_cast<const T*>(dfc), static_cast<T*>(dwg), static_cast<T*>(dwfc),
+                       wsp, M, K, N, p.tn / 2, p.tiles, p.rows, nitems);
+  else
+    hipLaunchKernelGGL((w_stage_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       static_cast<const T*>(x), static_cast<const T*>(dg),
+                       static_cast<const T*>(dfc), static_cast<T*>(dwg), static_cast<T*>(dwfc),
+                       wsp, M, K, N, p.tn / 2, p.tiles, p.rows, nitems);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   int64_t blocks = ceil_div(K * 2 * N / 4, 256);
