@@ -443,8 +443,9 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
 // operand panel of a tile, dg or dfc half) is formed once per tile; the column of the
 // double stage goes into the scalar soffset; the per-lane voffset (row and swizzled chunk)
 // is fixed.  The hardware range check applies to voffset only, against the window's rows,
-// so rows past the end still read zeros.  Only when N is not a multiple of 64 does the
-// last double stage of each half need a per-lane column test (template RAGGED).
+// so rows past the end still read zeros.  Only when some double stage reaches past N
+// (N not a multiple of 64, or N = 64) does a per-lane column test remain (template
+// RAGGED).
 struct XTile {   // first row of the dg/dfc panel and of the W panel; 32-bit (M < 2^31)
   int p0, q0;
   bool live;
@@ -1030,7 +1031,87 @@ __device__ inline void f_store_pair(float v0, float v1, uint32_t sel, __amdgpu_b
   if (ok) __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)voff, 0, 0);
 }
 
-template <typename T>
+// One forward issue: the tile's x window with the stage's first column as soffset, the
+// stage's k-row windows of W_g and W_fc with the tile's first column as soffset.
+struct FIssue {
+  __amdgpu_buffer_rsrc_t ra, rg, rf;
+  uint32_t sa, sw;
+  int kleft, nleft;
+  const uint16_t* dst;
+  const uint16_t* dstw;
+};
+
+template <bool RAGGED, int E>
+__device__ inline void f_dma(const FIssue& is, const uint32_t (&roff)[4], const int (&lcol)[4],
+                             const uint32_t (&wbase)[2], const int (&wcol)[2]) {
+  if (E < 4) {
+    constexpr int i = E;
+    const uint32_t v = !RAGGED || lcol[i] < is.kleft ? roff[i] : kOOB;
+    dma16s<i * 16 * BR * 2>(is.ra, v, is.sa, is.dst);
+  } else {
+    constexpr int t = E & 1;
+    const uint32_t v = !RAGGED || wcol[t] < is.nleft ? wbase[t] : kOOB;
+    if (E < 6) dma16s<t * 4 * FN * 2>(is.rg, v, is.sw, is.dstw);
+    else dma16s<BR * FN * 2 + t * 4 * FN * 2>(is.rf, v, is.sw, is.dstw);
+  }
+}
+
+template <bool RAGGED>
+__device__ inline void f_issue_all(const FIssue& is, const uint32_t (&roff)[4],
+                                   const int (&lcol)[4], const uint32_t (&wbase)[2],
+                                   const int (&wcol)[2]) {
+  f_dma<RAGGED, 0>(is, roff, lcol, wbase, wcol);
+  f_dma<RAGGED, 1>(is, roff, lcol, wbase, wcol);
+  f_dma<RAGGED, 2>(is, roff, lcol, wbase, wcol);
+  f_dma<RAGGED, 3>(is, roff, lcol, wbase, wcol);
+  f_dma<RAGGED, 4>(is, roff, lcol, wbase, wcol);
+  f_dma<RAGGED, 5>(is, roff, lcol, wbase, wcol);
+  f_dma<RAGGED, 6>(is, roff, lcol, wbase, wcol);
+  f_dma<RAGGED, 7>(is, roff, lcol, wbase, wcol);
+}
+
+// Fragment G (0..15, f_read's order: kk = G / 8; G % 8 < 4: x block G % 4, else W block
+// G % 4, the first two of W_g, the last two of W_fc).
+template <typename T, int G>
+__device__ inline void f_read_one(const uint16_t* slot, int wp, int lane, const int (&boff)[2],
+                                  FragSet<T>& f) {
+  using F = typename Mfma<T>::frag;
+  constexpr int kk = G / 8, blk = G % 4;
+  if (G % 8 < 4) {
+    const int lc = 2 * kk + (lane >> 5);
+    const int r = wp * 128 + blk * 32 + (lane & 31);
+    f.a[kk][blk] = *reinterpret_cast<const F*>(slot + r * BR + ((lc ^ xsw(r)) << 3));
+  } else {
+    f.b[kk][blk] = tr_frag<T, FN>(slot + BP * BR + (blk >= 2 ? BR * FN : 0) + 16 * kk * FN +
+                                  boff[blk & 1]);
+  }
+}
+
+template <typename T, bool RAGGED, bool READ_NEXT, int G>
+__device__ inline void f_group(f32x16 (&acc)[FP][FQ], const FragSet<T>& f, FragSet<T>& fn,
+                               const uint16_t* next_slot, int wp, int lane, const int (&boff)[2],
+                               const FIssue& is, const uint32_t (&roff)[4], const int (&lcol)[4],
+                               const uint32_t (&wbase)[2], const int (&wcol)[2]) {
+  constexpr int kk = G >> 3, i = (G >> 1) & 3, j = (G & 1) * 2;
+  acc[i][j] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j], acc[i][j]);
+  acc[i][j + 1] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j + 1], acc[i][j + 1]);
+  if (READ_NEXT) f_read_one<T, G>(next_slot, wp, lane, boff, fn);
+  if (G & 1) f_dma<RAGGED, (G >> 1)>(is, roff, lcol, wbase, wcol);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename T, bool RAGGED, bool READ_NEXT, int... G>
+__device__ inline void f_groups(std::integer_sequence<int, G...>, f32x16 (&acc)[FP][FQ],
+                                const FragSet<T>& f, FragSet<T>& fn, const uint16_t* next_slot,
+                                int wp, int lane, const int (&boff)[2], const FIssue& is,
+                                const uint32_t (&roff)[4], const int (&lcol)[4],
+                                const uint32_t (&wbase)[2], const int (&wcol)[2]) {
+  (f_group<T, RAGGED, READ_NEXT, G>(acc, f, fn, next_slot, wp, lane, boff, is, roff, lcol, wbase,
+                                     wcol),
+   ...);
+}
+
+template <typename T, bool RAGGED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_kernel(
     const T* __restrict__ x, const T* __restrict__ wg, const T* __restrict__ wfc,
     const T* __restrict__ bg, const T* __restrict__ bfc, T* __restrict__ g, T* __restrict__ fc,
@@ -1053,8 +1134,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 64 * wave + 16 * i + (lane >> 2);
-    roff[i] = (uint32_t)row * (uint32_t)(K * 2);
     lcol[i] = ((lane & 3) ^ xsw(row)) * 8;
+    roff[i] = (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)lcol[i] * 2u;
   }
   uint32_t wbase[2];
   int wcol[2];
@@ -1070,29 +1151,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int rows_a = c.live ? ((int)M - c.p0 < BP ? (int)M - c.p0 : BP) : 0;
     const int rows_w = c.live ? ((int)K - k0 < BR ? (int)K - k0 : BR) : 0;
     const int64_t kb = rows_w > 0 ? k0 : 0;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(x + (int64_t)c.p0 * K, clamp_bytes(rows_a, K * 2));
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(wg + kb * N, clamp_bytes(rows_w, N * 2));
-    const __amdgpu_buffer_rsrc_t rf = make_rsrc(wfc + kb * N, clamp_bytes(rows_w, N * 2));
-    uint32_t off[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = k0 + lcol[i];
-      off[i] = col < (int)K ? roff[i] + (uint32_t)(col * 2) : kOOB;
-    }
-    const int nleft = (int)N - c.n0;
-    const uint32_t n2 = (uint32_t)c.n0 * 2u;
-    const uint32_t wo0 = wcol[0] < nleft ? wbase[0] + n2 : kOOB;
-    const uint32_t wo1 = wcol[1] < nleft ? wbase[1] + n2 : kOOB;
-    const uint16_t* dst = slot + 64 * wave * BR;
-    const uint16_t* dstw = slot + BP * BR + 8 * wave * FN;
-    dma16<0 * 16 * BR * 2>(ra, off[0], dst);
-    dma16<1 * 16 * BR * 2>(ra, off[1], dst);
-    dma16<2 * 16 * BR * 2>(ra, off[2], dst);
-    dma16<3 * 16 * BR * 2>(ra, off[3], dst);
-    dma16<0 * 4 * FN * 2>(rg, wo0, dstw);
-    dma16<1 * 4 * FN * 2>(rg, wo1, dstw);
-    dma16<BR * FN * 2 + 0 * 4 * FN * 2>(rf, wo0, dstw);
-    dma16<BR * FN * 2 + 1 * 4 * FN * 2>(rf, wo1, dstw);
+    FIssue is;
+    is.ra = make_rsrc(uniform_ptr(x + (int64_t)c.p0 * K),
+                      __builtin_amdgcn_readfirstlane(clamp_bytes(rows_a, K * 2)));
+    const uint32_t wbytes = __builtin_amdgcn_readfirstlane(clamp_bytes(rows_w, N * 2));
+    is.rg = make_rsrc(uniform_ptr(wg + kb * N), wbytes);
+    is.rf = make_rsrc(uniform_ptr(wfc + kb * N), wbytes);
+    is.sa = __builtin_amdgcn_readfirstlane((uint32_t)k0 * 2u);
+    is.sw = __builtin_amdgcn_readfirstlane((uint32_t)c.n0 * 2u);
+    is.kleft = (int)K - k0;
+    is.nleft = (int)N - c.n0;
+    is.dst = slot + 64 * wave * BR;
+    is.dstw = slot + BP * BR + 8 * wave * FN;
+    return is;
   };
   // transposing-read offsets of this wave's two 32-column blocks (see w_lane_offsets)
   int boff[2];
@@ -1105,18 +1176,48 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int j = 0; j < 2; ++j)
       boff[j] = row * FN + (((4 * (2 * wq + j) + q) ^ sw) << 3) + 4 * (sl & 1);
   }
-#define F_ISSUE(c, s, slot) issue((c), (s), (slot))
 #define F_READ(slot, f) f_read<T>((slot), wp, lane, boff, (f))
-  constexpr int READS_PER_STEP = 24;   // 8 ds_read_b128 + 16 ds_read_b64_tr_b16
+  // one pipeline step u (0..3), loads and next-stage reads spread between the MFMAs
+#define F_STEP(ctx, st, u, READ_NEXT)                                                       \
+  do {                                                                                    \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));                            \
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                                \
+    SWG_COMPILER_FENCE();                                                                 \
+    __builtin_amdgcn_s_barrier();                                                         \
+    SWG_COMPILER_FENCE();                                                                 \
+    const FIssue is_ = issue((ctx), (st), ring + (u) * SLOT);                              \
+    f_groups<T, RAGGED, (READ_NEXT)>(std::make_integer_sequence<int, 16>{}, acc,           \
+                                     frags[(u) & 1], frags[((u) + 1) & 1],                \
+                                     ring + (((u) + 1) & 3) * SLOT, wp, lane, boff, is_,   \
+                                     roff, lcol, wbase, wcol);                            \
+  } while (0)
 
   f32x16 acc[FP][FQ];
   FragSet<T> frags[2];
   FTile cur = f_tile(f0, my_tiles > 0, nn);
-  SWG_PIPE_PROLOGUE(F_ISSUE, cur);
+  f_issue_all<RAGGED>(issue(cur, 0, ring), roff, lcol, wbase, wcol);
+  f_issue_all<RAGGED>(issue(cur, 1, ring + SLOT), roff, lcol, wbase, wcol);
+  f_issue_all<RAGGED>(issue(cur, 2, ring + 2 * SLOT), roff, lcol, wbase, wcol);
+  f_issue_all<RAGGED>(issue(cur, 3, ring + 3 * SLOT), roff, lcol, wbase, wcol);
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * LOADS_PER_STAGE));
+  SWG_COMPILER_FENCE();
+  __builtin_amdgcn_s_barrier();
+  SWG_COMPILER_FENCE();
   for (int64_t j = 0; j < my_tiles; ++j) {
     const FTile nxt = f_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nn);
     zero_acc(acc);
-    SWG_TILE_ROUNDS(F_ISSUE, F_READ, frags, cur, nxt, nst);
+    F_READ(ring, frags[0]);
+    int64_t t = 0;
+    for (; t + 4 < nst; t += 4) {
+      F_STEP(cur, t + 4, 0, true);
+      F_STEP(cur, t + 5, 1, true);
+      F_STEP(cur, t + 6, 2, true);
+      F_STEP(cur, t + 7, 3, true);
+    }
+    F_STEP(nxt, 0, 0, true);
+    F_STEP(nxt, 1, 1, true);
+    F_STEP(nxt, 2, 2, true);
+    F_STEP(nxt, 3, 3, false);   // the next tile's first stage is read after the epilogue
     // epilogue: bias, SiLU, product, three outputs
     {
       int ln = lane;
@@ -1156,7 +1257,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
     cur = nxt;
   }
-#undef F_ISSUE
+#undef F_STEP
 #undef F_READ
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
@@ -1168,7 +1269,9 @@ static hipError_t x_stage_t(const void* dg, const void* dfc, const void* wg, con
   const int64_t np = ceil_div(M, BP), nq = ceil_div(K, BQ);
   const int64_t ntiles = np * nq;
   const int64_t grid = ntiles < cus ? ntiles : cus;
-  if (N % XA_BR == 0)
+  // per-lane column tests unless every double stage is whole: N a multiple of 64 and at
+  // least two double stages per half (N = 64 pads the half with a stage past N)
+  if (N % XA_BR == 0 && N >= 2 * XA_BR)
     hipLaunchKernelGGL((x_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        static_cast<const T*>(dg), static_cast<const T*>(dfc),
                        static_cast<const T*>(wg), static_cast<const T*>(wfc),
@@ -1195,6 +1298,7 @@ static hipError_t w_stage_t(const WPlan& p, const void* x, const void* dg, const
   float* wsp = p.splits > 1 ? ws : nullptr;
   const int64_t nitems = p.splits * p.tiles;
   const int64_t grid = nitems < cus ? nitems : cus;
+  // per-lane column tests only for tiles cut by the right or bottom edge of dW
   if (K % BP == 0 && N % BQ == 0)
     hipLaunchKernelGGL((w_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        static_cast<const T*>(x), static_cast<const T*>(dg),
@@ -1228,11 +1332,20 @@ static hipError_t fwd_t(const void* x, const void* wg, const void* wfc, const vo
   const int64_t np = ceil_div(M, BP), nn = ceil_div(N, FN);
   const int64_t ntiles = np * nn;
   const int64_t grid = ntiles < cus ? ntiles : cus;
-  hipLaunchKernelGGL((fwd_kernel<T>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                     static_cast<const T*>(x), static_cast<const T*>(wg),
-                     static_cast<const T*>(wfc), static_cast<const T*>(bg),
-                     static_cast<const T*>(bfc), static_cast<T*>(g), static_cast<T*>(fc),
-                     static_cast<T*>(y), M, K, N, nn, ntiles);
+  // per-lane column tests unless every stage is whole: K a multiple of a ring round
+  // (stages past K would otherwise read the next row of x) and N of the tile width
+  if (K % (4 * BR) == 0 && N % FN == 0)
+    hipLaunchKernelGGL((fwd_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       static_cast<const T*>(x), static_cast<const T*>(wg),
+                       static_cast<const T*>(wfc), static_cast<const T*>(bg),
+                       static_cast<const T*>(bfc), static_cast<T*>(g), static_cast<T*>(fc),
+                       static_cast<T*>(y), M, K, N, nn, ntiles);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       static_cast<const T*>(x), static_cast<const T*>(wg),
+                       static_cast<const T*>(wfc), static_cast<const T*>(bg),
+                       static_cast<const T*>(bfc), static_cast<T*>(g), static_cast<T*>(fc),
+                       static_cast<T*>(y), M, K, N, nn, ntiles);
   return hipGetLastError();
 }
 

@@ -70,7 +70,8 @@ def test_forward_workloads(wl, dt):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 8, 8), (63, 72, 136), (300, 264, 264), (257, 520, 8),
-                                   (700, 256, 128), (513, 1032, 72), (2000, 64, 2048)])
+                                   (700, 256, 128), (513, 1032, 72), (2000, 64, 2048),
+                                   (300, 96, 64), (520, 384, 256)])
 def test_forward_odd_shapes(M, K, N):
     inp = swiglu_inputs(SwiGLUShape("odd", 17, M, K, N), with_forward=False)
     _fwd_case(inp, "bf16")

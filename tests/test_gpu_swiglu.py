@@ -134,7 +134,7 @@ def test_x_stage_workloads(wl, dt):
 
 @pytest.mark.parametrize("M,K,N", [(1, 8, 8), (63, 72, 136), (300, 264, 264), (1000, 8, 520),
                                    (257, 520, 8), (700, 256, 128), (513, 1032, 72),
-                                   (2000, 64, 2048)])
+                                   (2000, 64, 2048), (300, 200, 64), (129, 96, 192)])
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
 def test_gemm_stages_odd_shapes(M, K, N, dt):
     inp = swiglu_inputs(SwiGLUShape("odd", 13, M, K, N), dtype=dt)
