@@ -349,10 +349,11 @@ __device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane_in, F
 // columns into one row each (pack to 16 bits, swap the packed words with the neighbouring
 // lane, byte-permute: even lanes keep row R, odd lanes row R + 1) and writes 32 bits per
 // row.  `r` is a buffer window over the tile's valid rows only, so stores to rows past the
-// output are dropped by the hardware range check; columns are checked only when the tile
-// is cut by the output's right edge (cols_left < 256: columns left from the tile's first;
-// a multiple of 8, so a pair never straddles it).  wrow0 / wcol0: the wave's first row /
-// column inside the tile.  All offsets are 32-bit (256 rows x 2^23 bytes < 2^31).
+// output are dropped by the hardware range check, and so are stores to columns past the
+// output's right edge, whose offsets are pushed out of the window (cols_left: columns left
+// from the tile's first; a multiple of 8, so a pair never straddles it).  wrow0 / wcol0:
+// the wave's first row / column inside the tile.  All offsets are 32-bit (256 rows x 2^23
+// bytes < 2^31).
 template <typename T>
 __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
                                        __amdgpu_buffer_rsrc_t r, uint32_t row_bytes, int wrow0,
@@ -363,23 +364,37 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
                   (uint32_t)(wcol0 + ((lane & 31) & ~1)) * 2u;
   asm volatile("" : "+v"(loff));   // keeps the 32 row offsets below from being hoisted out of
                                    // the tile loop (they would stay live, and spill)
+  // columns past the tensor's edge: the offset is pushed past the window and the store is
+  // dropped by the range check (no branch per store)
+  uint32_t cbad[FQ];
+#pragma unroll
+  for (int j = 0; j < FQ; ++j) {
+    cbad[j] = wcol0 + j * 32 + ((lane & 31) & ~1) < cols_left ? 0u : kOOB;
+    asm volatile("" : "+v"(cbad[j]));   // formed here, not hoisted (see loff)
+  }
+  asm volatile("" : "+s"(row_bytes));  // the row offsets below likewise
+  // An always-true wave-uniform test the compiler cannot fold: each row pair's stores sit
+  // in a block of their own, so the accumulators are copied out a few at a time (in
+  // straight-line code the copies of all 256 are hoisted together, and spill).
+  int go = 1;
+  asm volatile("" : "+s"(go));
 #pragma unroll
   for (int i = 0; i < FP; ++i) {
 #pragma unroll
     for (int rr = 0; rr < 16; rr += 2) {
-      const uint32_t voff = loff + (uint32_t)(wrow0 + i * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes;
+      asm volatile("" : "+s"(go));   // a fresh value per block (no threading of the tests)
+      if (go) {
+        const uint32_t voff =
+            loff + (uint32_t)(wrow0 + i * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes;
 #pragma unroll
-      for (int j = 0; j < FQ; ++j) {
-        const uint32_t own = pack2<T>(acc[i][j][rr], acc[i][j][rr + 1]);
-        const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
-        const uint32_t out = __builtin_amdgcn_perm(nb, own, sel);
-        if (cols_left >= BQ || wcol0 + j * 32 + ((lane & 31) & ~1) < cols_left)
-          __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)(voff + 64u * j), 0, 0);
+        for (int j = 0; j < FQ; ++j) {
+          const uint32_t own = pack2<T>(acc[i][j][rr], acc[i][j][rr + 1]);
+          const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
+          const uint32_t out = __builtin_amdgcn_perm(nb, own, sel);
+          __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)((voff | cbad[j]) + 64u * j), 0, 0);
+        }
       }
     }
-    // keep the scheduler from hoisting every accumulator read to the top (the copies
-    // would need more registers than the tile loop has free, and spill)
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -692,6 +707,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       wc = wn;
       wn = x_win(nxt, M, K, N);
     }
+    __builtin_amdgcn_sched_barrier(0);   // the epilogue stays ahead of the next reads
     zero_acc(acc);
     X_READ(0, ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, frags[0]);   // stage 0
     int d0 = 0;
