@@ -135,6 +135,28 @@ swg_status swiglu_fwd(const void* x, const void* w_g, const void* w_fc,
 swg_status swish_grad(const void* grad, const void* x, void* grad_x, int64_t n,
                       swg_dtype dtype, const float* beta, void* stream);
 
+/*
+ * Swish gradient over strided (non-contiguous) tensors [Swish page, sections 3.5 and 4.2:
+ * non-contiguous inputs are accepted, tensors of more than 8 dimensions are flattened,
+ * and the result is written into a possibly non-contiguous output].  The three tensors
+ * share one logical shape sizes[0..ndim) (row-major order; ndim 0 is a scalar, up to
+ * SWG_MAX_NDIM dimensions); grad_strides, x_strides and out_strides give each tensor's
+ * element strides per dimension (host arrays; negative strides allowed; input strides
+ * may be 0, i.e. broadcast views).  The pointers address each tensor's element at
+ * logical index (0, ..., 0).  Dimensions that are contiguous in all three tensors are
+ * merged first; a view that is contiguous after merging runs the contiguous kernel.
+ * Errors: SWG_ERR_INVALID for a negative size, an element count that overflows int64,
+ * misaligned pointers, an output whose elements overlap each other, or an output that
+ * overlaps an input other than as the exact same view (same pointer and strides, which
+ * is in-place); SWG_ERR_UNSUPPORTED when more than 8 dimensions remain after merging.
+ * Empty views (a size of 0) return SWG_OK without touching the pointers.
+ */
+#define SWG_MAX_NDIM 64
+swg_status swish_grad_strided(const void* grad, const void* x, void* grad_x, int ndim,
+                              const int64_t* sizes, const int64_t* grad_strides,
+                              const int64_t* x_strides, const int64_t* out_strides,
+                              swg_dtype dtype, const float* beta, void* stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* swg_status_string(int status);
 

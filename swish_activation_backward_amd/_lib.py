@@ -13,9 +13,10 @@ import threading
 
 import torch
 
-__all__ = ["SwgError", "load_library", "library_path", "swish_grad", "swiglu_bwd_b",
-           "swiglu_bwd_w", "swiglu_bwd_x", "swiglu_fwd", "swiglu_bwd_b_workspace_size",
-           "swiglu_bwd_w_workspace_size", "swg_version", "DTYPE_CODE", "STATUS"]
+__all__ = ["SwgError", "load_library", "library_path", "swish_grad", "swish_grad_strided",
+           "swiglu_bwd_b", "swiglu_bwd_w", "swiglu_bwd_x", "swiglu_fwd",
+           "swiglu_bwd_b_workspace_size", "swiglu_bwd_w_workspace_size", "swg_version",
+           "DTYPE_CODE", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libswiglu_bwd.so"
@@ -56,6 +57,10 @@ def load_library():
         vp, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
         lib.swish_grad.argtypes = [vp, vp, vp, i64, i32, ctypes.POINTER(ctypes.c_float), vp]
         lib.swish_grad.restype = i32
+        pi64 = ctypes.POINTER(ctypes.c_int64)
+        lib.swish_grad_strided.argtypes = [vp, vp, vp, i32, pi64, pi64, pi64, pi64, i32,
+                                           ctypes.POINTER(ctypes.c_float), vp]
+        lib.swish_grad_strided.restype = i32
         lib.swiglu_bwd_b.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]
         lib.swiglu_bwd_b.restype = i32
         lib.swiglu_bwd_b_workspace_size.argtypes = [i64, i64, i32]
@@ -133,20 +138,51 @@ def swg_version() -> str:
     return load_library().swg_version().decode()
 
 
+def _same_kind(name, t, dtype, shape, device):
+    """dtype, shape and device checks without a layout requirement (strided calls)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 def swish_grad(grad, x, grad_x=None, beta=None, stream=None):
-    """grad_x = grad * sigma(beta x) * (1 + beta x (1 - sigma(beta x)))  (1-D view of any
-    shape).  ``beta`` None means 1.0; ``grad_x`` may be ``grad`` or ``x`` (in place)."""
-    lib = load_library()
-    _dense("x", x, grad.dtype, grad.shape, grad.device)
-    if not grad.is_contiguous():
-        raise ValueError("grad must be contiguous")
+    """grad_x = grad * sigma(beta x) * (1 + beta x (1 - sigma(beta x)))  (elementwise, any
+    shape).  ``beta`` None means 1.0; ``grad_x`` may be ``grad`` or ``x`` (in place).
+    Contiguous tensors go to ``swish_grad``; any other layout (transposed, sliced,
+    broadcast inputs, a non-contiguous output) to ``swish_grad_strided``."""
+    _same_kind("x", x, grad.dtype, grad.shape, grad.device)
     if grad_x is None:
-        grad_x = torch.empty_like(grad)
-    _dense("grad_x", grad_x, grad.dtype, grad.shape, grad.device)
+        grad_x = torch.empty(grad.shape, dtype=grad.dtype, device=grad.device)
+    _same_kind("grad_x", grad_x, grad.dtype, grad.shape, grad.device)
+    if not (grad.is_contiguous() and x.is_contiguous() and grad_x.is_contiguous()):
+        return swish_grad_strided(grad, x, grad_x, beta=beta, stream=stream)
+    lib = load_library()
     b = None if beta is None else ctypes.byref(ctypes.c_float(beta))
     st = lib.swish_grad(_ptr(grad), _ptr(x), _ptr(grad_x), grad.numel(), _dtype_code(grad), b,
                         _stream(stream))
     _check("swish_grad", st, lib)
+    return grad_x
+
+
+def swish_grad_strided(grad, x, grad_x, beta=None, stream=None):
+    """The Swish gradient over tensors of one shape with any strides (the C entry point
+    of the same name: passes torch's sizes and element strides)."""
+    _same_kind("x", x, grad.dtype, grad.shape, grad.device)
+    _same_kind("grad_x", grad_x, grad.dtype, grad.shape, grad.device)
+    lib = load_library()
+    nd = grad.dim()
+    arr = ctypes.c_int64 * max(nd, 1)
+    sizes = arr(*grad.shape)
+    sg, sx, so = arr(*grad.stride()), arr(*x.stride()), arr(*grad_x.stride())
+    b = None if beta is None else ctypes.byref(ctypes.c_float(beta))
+    st = lib.swish_grad_strided(_ptr(grad), _ptr(x), _ptr(grad_x), nd, sizes, sg, sx, so,
+                                _dtype_code(grad), b, _stream(stream))
+    _check("swish_grad_strided", st, lib)
     return grad_x
 
 

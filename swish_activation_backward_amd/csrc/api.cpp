@@ -95,6 +95,113 @@ swg_status swish_grad(const void* grad, const void* x, void* grad_x, int64_t n, 
   return hip_status(launch_swish_grad(dtype, grad, x, grad_x, n, b, vec, as_stream(stream)));
 }
 
+// ------------------------------------------------------------------- strided swish_grad
+swg_status swish_grad_strided(const void* grad, const void* x, void* grad_x, int ndim,
+                              const int64_t* sizes, const int64_t* grad_strides,
+                              const int64_t* x_strides, const int64_t* out_strides,
+                              swg_dtype dtype, const float* beta, void* stream) {
+  if (!dtype_ok(dtype) || ndim < 0 || ndim > SWG_MAX_NDIM) return SWG_ERR_INVALID;
+  if (ndim > 0 && (!sizes || !grad_strides || !x_strides || !out_strides))
+    return SWG_ERR_NULLPTR;
+  int64_t n = 1;
+  for (int d = 0; d < ndim; ++d) {
+    if (sizes[d] < 0) return SWG_ERR_INVALID;
+    if (__builtin_mul_overflow(n, sizes[d], &n)) return SWG_ERR_INVALID;
+  }
+  if (n == 0) return SWG_OK;
+  if (!grad || !x || !grad_x) return SWG_ERR_NULLPTR;
+  const int64_t es = elem_size(dtype);
+  if (!aligned(grad, (size_t)es) || !aligned(x, (size_t)es) || !aligned(grad_x, (size_t)es))
+    return SWG_ERR_INVALID;
+  const int64_t* st[3] = {grad_strides, x_strides, out_strides};
+
+  // the output's elements must not overlap each other: with its dimensions of size > 1
+  // sorted by |stride|, each stride must exceed the extent spanned by the smaller ones
+  {
+    int64_t ord[SWG_MAX_NDIM];
+    int m = 0;
+    for (int d = 0; d < ndim; ++d)
+      if (sizes[d] > 1) {
+        const int64_t a = out_strides[d] < 0 ? -out_strides[d] : out_strides[d];
+        int k = m++;
+        while (k > 0) {
+          const int64_t b = out_strides[ord[k - 1]] < 0 ? -out_strides[ord[k - 1]]
+                                                       : out_strides[ord[k - 1]];
+          if (b <= a) break;
+          ord[k] = ord[k - 1];
+          --k;
+        }
+        ord[k] = d;
+      }
+    int64_t extent = 0;
+    for (int k = 0; k < m; ++k) {
+      const int d = (int)ord[k];
+      const int64_t a = out_strides[d] < 0 ? -out_strides[d] : out_strides[d];
+      if (a <= extent) return SWG_ERR_INVALID;
+      int64_t span;
+      if (__builtin_mul_overflow(sizes[d] - 1, a, &span) ||
+          __builtin_add_overflow(extent, span, &extent))
+        return SWG_ERR_INVALID;
+    }
+  }
+  // byte span [lo, hi] of each view; the output may meet an input only as the same view
+  {
+    auto span = [&](const void* p, const int64_t* s, intptr_t& lo, intptr_t& hi) {
+      int64_t a = 0, b = 0;
+      for (int d = 0; d < ndim; ++d) {
+        const int64_t e = (sizes[d] - 1) * s[d];
+        if (e < 0) a += e; else b += e;
+      }
+      lo = reinterpret_cast<intptr_t>(p) + (intptr_t)(a * es);
+      hi = reinterpret_cast<intptr_t>(p) + (intptr_t)(b * es) + (intptr_t)es - 1;
+    };
+    intptr_t olo, ohi;
+    span(grad_x, out_strides, olo, ohi);
+    const void* ins[2] = {grad, x};
+    for (int t = 0; t < 2; ++t) {
+      intptr_t lo, hi;
+      span(ins[t], st[t], lo, hi);
+      if (lo > ohi || olo > hi) continue;   // disjoint
+      bool same = ins[t] == grad_x;
+      for (int d = 0; same && d < ndim; ++d) same = sizes[d] == 1 || st[t][d] == out_strides[d];
+      if (!same) return SWG_ERR_INVALID;
+    }
+  }
+  // merge dimensions (innermost first) that are contiguous in all three tensors; drop
+  // dimensions of size 1
+  StridedView v;
+  int64_t msize[SWG_MAX_NDIM], mst[3][SWG_MAX_NDIM];
+  int nd = 0;
+  for (int d = ndim - 1; d >= 0; --d) {
+    if (sizes[d] == 1) continue;
+    if (nd > 0) {
+      const int c = nd - 1;
+      bool merge = true;
+      for (int t = 0; t < 3; ++t) merge = merge && st[t][d] == mst[t][c] * msize[c];
+      if (merge) {
+        msize[c] *= sizes[d];
+        continue;
+      }
+    }
+    msize[nd] = sizes[d];
+    for (int t = 0; t < 3; ++t) mst[t][nd] = st[t][d];
+    ++nd;
+  }
+  const float b = beta ? *beta : 1.0f;
+  if (nd == 0 || (nd == 1 && mst[0][0] == 1 && mst[1][0] == 1 && mst[2][0] == 1)) {
+    const bool vec = aligned(grad, 16) && aligned(x, 16) && aligned(grad_x, 16);
+    return hip_status(launch_swish_grad(dtype, grad, x, grad_x, n, b, vec, as_stream(stream)));
+  }
+  if (nd > kMaxStridedDims) return SWG_ERR_UNSUPPORTED;
+  v.nd = nd;
+  for (int k = 0; k < nd; ++k) {   // back to outermost-first order
+    v.size[k] = msize[nd - 1 - k];
+    for (int t = 0; t < 3; ++t) v.stride[t][k] = mst[t][nd - 1 - k];
+  }
+  return hip_status(launch_swish_grad_strided(dtype, grad, x, grad_x, v, n, b,
+                                              as_stream(stream)));
+}
+
 // ------------------------------------------------------------------- b stage
 size_t swiglu_bwd_b_workspace_size(int64_t M, int64_t N, swg_dtype dtype) {
   if (!dtype_ok(dtype) || M <= 0 || N <= 0) return 0;

@@ -13,6 +13,20 @@ constexpr int64_t kMaxStreamBlocks = 8192;
 hipError_t launch_swish_grad(int dtype, const void* grad, const void* x, void* out, int64_t n,
                              float beta, bool vector_path, hipStream_t stream);
 
+// Strided views for swish_grad: a logical shape in row-major order (after merging the
+// dimensions that are contiguous in all three tensors) and each tensor's element strides.
+constexpr int kMaxStridedDims = 8;
+struct StridedView {
+  int nd;
+  int64_t size[kMaxStridedDims];
+  int64_t stride[3][kMaxStridedDims];   // grad, x, grad_x
+};
+
+// grad_x[i] for every logical index i of the view (n = product of the sizes > 0)
+hipError_t launch_swish_grad_strided(int dtype, const void* grad, const void* x, void* out,
+                                     const StridedView& v, int64_t n, float beta,
+                                     hipStream_t stream);
+
 hipError_t launch_b_stage(int dtype, const BPlan& p, const void* dy, const void* g,
                           const void* fc, void* dg, void* dfc, void* db_g, void* db_fc,
                           int64_t M, int64_t N, float* part, hipStream_t stream);

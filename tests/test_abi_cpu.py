@@ -71,6 +71,41 @@ def test_swish_grad_argument_errors(lib):
     assert lib.swish_grad(P, Q, ctypes.c_void_p(0x20000 - 8), 100, BF16, beta, NULL) == INVALID
 
 
+def _i64(*v):
+    return (ctypes.c_int64 * max(len(v), 1))(*v)
+
+
+def test_swish_grad_strided_argument_errors(lib):
+    beta = ctypes.byref(ctypes.c_float(1.0))
+    f = lib.swish_grad_strided
+    c2 = _i64(4, 1)
+    assert f(P, Q, R, -1, _i64(4), _i64(1), _i64(1), _i64(1), BF16, beta, NULL) == INVALID
+    assert f(P, Q, R, 65, _i64(4), _i64(1), _i64(1), _i64(1), BF16, beta, NULL) == INVALID
+    assert f(P, Q, R, 2, _i64(3, 4), c2, c2, c2, 9, beta, NULL) == INVALID       # dtype
+    assert f(P, Q, R, 2, NULL, c2, c2, c2, BF16, beta, NULL) == NULLPTR
+    assert f(P, Q, R, 2, _i64(3, 4), NULL, c2, c2, BF16, beta, NULL) == NULLPTR
+    assert f(P, Q, R, 2, _i64(3, -4), c2, c2, c2, BF16, beta, NULL) == INVALID   # negative size
+    assert f(P, Q, R, 2, _i64(1 << 40, 1 << 40), c2, c2, c2, BF16, beta, NULL) == INVALID
+    # empty views succeed without looking at the pointers
+    assert f(NULL, NULL, NULL, 2, _i64(0, 4), c2, c2, c2, BF16, beta, NULL) == OK
+    assert f(NULL, Q, R, 2, _i64(3, 4), c2, c2, c2, BF16, beta, NULL) == NULLPTR
+    assert f(ctypes.c_void_p(0x10001), Q, R, 2, _i64(3, 4), c2, c2, c2, BF16, beta,
+             NULL) == INVALID                                                       # misaligned
+    # an output whose elements overlap: a zero stride, or strides that interleave
+    assert f(P, Q, R, 2, _i64(3, 4), c2, c2, _i64(0, 1), BF16, beta, NULL) == INVALID
+    assert f(P, Q, R, 2, _i64(4, 4), c2, c2, _i64(2, 1), BF16, beta, NULL) == INVALID
+    # broadcast (zero-stride) inputs are fine for validation; overlap of the output with
+    # an input other than the identical view is rejected
+    assert f(P, Q, ctypes.c_void_p(0x10000 + 4), 2, _i64(3, 4), c2, c2, c2, BF16, beta,
+             NULL) == INVALID
+    assert f(P, Q, P, 2, _i64(3, 4), _i64(1, 3), c2, c2, BF16, beta, NULL) == INVALID
+    # nine dimensions that cannot be merged (x runs the other way round)
+    sizes = _i64(*([2] * 9))
+    rowmajor = _i64(*[1 << (8 - d) for d in range(9)])
+    colmajor = _i64(*[1 << d for d in range(9)])
+    assert f(P, Q, R, 9, sizes, rowmajor, colmajor, rowmajor, BF16, beta, NULL) == UNSUPPORTED
+
+
 def test_b_stage_argument_errors(lib):
     ws = swg.swiglu_bwd_b_workspace_size
     import torch
@@ -176,6 +211,8 @@ def test_binding_checks_shapes_without_gpu():
     # well-formed host tensors are refused before any library call
     with pytest.raises(ValueError, match="GPU only"):
         swg.swish_grad(x, x)
+    with pytest.raises(ValueError, match="GPU only"):
+        swg.swish_grad(x.t(), x.t())        # non-contiguous: the strided entry point
     w = torch.zeros(8, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU only"):
         swg.swiglu_fwd(x, w, w, None, None, x.clone(), x.clone(), x.clone())
