@@ -81,12 +81,13 @@ size_t swiglu_bwd_b_workspace_size(int64_t M, int64_t N, swg_dtype dtype);
  * one GEMM [K, M] x [M, 2N] whose right operand is the column concatenation of dg and dfc.
  *   dw_g[k,n]  = RNE(dw_g[k,n]  + sum_m x[m,k] * dg[m,n])
  *   dw_fc[k,n] = RNE(dw_fc[k,n] + sum_m x[m,k] * dfc[m,n])
- * x: [M, K]; dg, dfc: [M, N]; dw_g, dw_fc: [K, N].  dtype: bf16 or fp16 (fp32 returns
- * SWG_ERR_UNSUPPORTED).  K and N must be multiples of 8 (16-byte rows) and below 2^22,
- * and M below 2^31, otherwise SWG_ERR_UNSUPPORTED.  Products are formed on the matrix cores, accumulated in fp32
- * (split over M in fixed-order fp32 partials when the output is small), added to the
- * current dw and rounded once: dw is ACCUMULATED like db.  `workspace` holds
- * swiglu_bwd_w_workspace_size(M, K, N, dtype) bytes (0 when no split is needed).
+ * x: [M, K]; dg, dfc: [M, N]; dw_g, dw_fc: [K, N].  dtype: bf16, fp16 or fp32.  K and N
+ * must be multiples of 8 (bf16 / fp16) or of 4 (fp32), i.e. 16-byte rows, and below 2^22,
+ * and M below 2^31, otherwise SWG_ERR_UNSUPPORTED.  Products are formed on the matrix
+ * cores, accumulated in fp32 (split over M in fixed-order fp32 partials when the output is
+ * small), added to the current dw and rounded once (fp32: not rounded): dw is ACCUMULATED
+ * like db.  `workspace` holds swiglu_bwd_w_workspace_size(M, K, N, dtype) bytes (0 when
+ * no split is needed; the same for every dtype).
  */
 swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc,
                         void* dw_g, void* dw_fc,
@@ -98,9 +99,9 @@ size_t swiglu_bwd_w_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dt
  * x stage [SwiGLU page, formula 4; kernel 3]:  dx = [dg | dfc] [W_g | W_fc]^T
  * one GEMM [M, 2N] x [2N, K]:  dx[m,k] = sum_n dg[m,n] W_g[k,n] + dfc[m,n] W_fc[k,n].
  * dg, dfc: [M, N]; w_g, w_fc: [K, N] (row-major, as on the page); dx: [M, K], OVERWRITTEN.
- * dtype: bf16 or fp16; K and N multiples of 8 and below 2^22, M below 2^31 (else
- * SWG_ERR_UNSUPPORTED).  fp32
- * accumulation, one rounding.  N = 0 with M*K > 0 writes dx = 0 (the empty sum).
+ * dtype: bf16, fp16 or fp32; K and N multiples of 8 (bf16 / fp16) or of 4 (fp32) and
+ * below 2^22, M below 2^31 (else SWG_ERR_UNSUPPORTED).  fp32 accumulation, one rounding
+ * (none for fp32).  N = 0 with M*K > 0 writes dx = 0 (the empty sum).
  */
 swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
                         void* dx, int64_t M, int64_t K, int64_t N, swg_dtype dtype,

@@ -229,10 +229,14 @@ swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc, void* dg,
 }
 
 // ------------------------------------------------------------------- GEMM stages
-static swg_status gemm_shape_check(int dtype, int64_t M, int64_t K, int64_t N) {
+// fp32_ok: the w and x stages have an fp32 path (K, N multiples of 4: 16-byte vectors);
+// the 16-bit paths need K, N multiples of 8.
+static swg_status gemm_shape_check(int dtype, int64_t M, int64_t K, int64_t N,
+                                   bool fp32_ok = false) {
   if (!dtype_ok(dtype) || M < 0 || K < 0 || N < 0) return SWG_ERR_INVALID;
-  if (dtype == SWG_FP32) return SWG_ERR_UNSUPPORTED;
-  if (K % 8 != 0 || N % 8 != 0) return SWG_ERR_UNSUPPORTED;
+  if (dtype == SWG_FP32 && !fp32_ok) return SWG_ERR_UNSUPPORTED;
+  const int64_t vec = dtype == SWG_FP32 ? 4 : 8;
+  if (K % vec != 0 || N % vec != 0) return SWG_ERR_UNSUPPORTED;
   // tile windows are addressed with 32-bit byte offsets (256 rows of 2N bytes) and
   // row indices in 32 bits
   if (K >= kMaxGemmDim || N >= kMaxGemmDim || M >= (int64_t(1) << 31)) return SWG_ERR_UNSUPPORTED;
@@ -240,14 +244,14 @@ static swg_status gemm_shape_check(int dtype, int64_t M, int64_t K, int64_t N) {
 }
 
 size_t swiglu_bwd_w_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dtype) {
-  if (gemm_shape_check(dtype, M, K, N) != SWG_OK || M == 0 || K == 0 || N == 0) return 0;
+  if (gemm_shape_check(dtype, M, K, N, true) != SWG_OK || M == 0 || K == 0 || N == 0) return 0;
   return plan_w(M, K, N).ws_bytes;
 }
 
 swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc, void* dw_g, void* dw_fc,
                         int64_t M, int64_t K, int64_t N, swg_dtype dtype, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  swg_status st = gemm_shape_check(dtype, M, K, N);
+  swg_status st = gemm_shape_check(dtype, M, K, N, true);
   if (st != SWG_OK) return st;
   if (M == 0 || K == 0 || N == 0) return SWG_OK;  // dw += empty sum
   if (!x || !dg || !dfc || !dw_g || !dw_fc) return SWG_ERR_NULLPTR;
@@ -264,13 +268,14 @@ swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc, void* dw
 
 swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
                         void* dx, int64_t M, int64_t K, int64_t N, swg_dtype dtype, void* stream) {
-  swg_status st = gemm_shape_check(dtype, M, K, N);
+  swg_status st = gemm_shape_check(dtype, M, K, N, true);
   if (st != SWG_OK) return st;
   if (M == 0 || K == 0) return SWG_OK;  // dx is empty
   if (!dx) return SWG_ERR_NULLPTR;
   if (!aligned(dx, 16)) return SWG_ERR_UNSUPPORTED;
   if (N == 0)  // the empty sum: dx = 0
-    return hip_status(launch_zero(dx, (size_t)M * (size_t)K * 2, as_stream(stream)));
+    return hip_status(launch_zero(dx, (size_t)M * (size_t)K * (size_t)elem_size(dtype),
+                                  as_stream(stream)));
   if (!dg || !dfc || !w_g || !w_fc) return SWG_ERR_NULLPTR;
   for (const void* p : {dg, dfc, w_g, w_fc}) if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
   return hip_status(launch_x_stage(dtype, dg, dfc, w_g, w_fc, dx, M, K, N, gemm_grid_cap(),

@@ -955,8 +955,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
-// dw = RNE(dw + sum_s ws[s]) in split order; 4 consecutive columns per lane (N % 8 == 0,
-// so a group never straddles the dg | dfc boundary).
+// dw = RNE(dw + sum_s ws[s]) in split order (fp32 dw: no rounding); 4 consecutive columns
+// per lane (N % 4 == 0, so a group never straddles the dg | dfc boundary).
 template <typename T>
 __global__ __launch_bounds__(256) void w_reduce_kernel(const float* __restrict__ ws,
                                                        T* __restrict__ dwg, T* __restrict__ dwfc,
@@ -1304,7 +1304,8 @@ hipError_t launch_x_stage(int dtype, const void* dg, const void* dfc, const void
                           const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
                           hipStream_t stream) {
   if (dtype == 0) return x_stage_t<bf16>(dg, dfc, w_g, w_fc, dx, M, K, N, cus, stream);
-  return x_stage_t<fp16>(dg, dfc, w_g, w_fc, dx, M, K, N, cus, stream);
+  if (dtype == 1) return x_stage_t<fp16>(dg, dfc, w_g, w_fc, dx, M, K, N, cus, stream);
+  return launch_x_stage32(dg, dfc, w_g, w_fc, dx, M, K, N, stream);
 }
 
 template <typename T>
@@ -1338,7 +1339,15 @@ hipError_t launch_w_stage(int dtype, const WPlan& p, const void* x, const void* 
                           const void* dfc, void* dw_g, void* dw_fc, int64_t M, int64_t K,
                           int64_t N, float* ws, int cus, hipStream_t stream) {
   if (dtype == 0) return w_stage_t<bf16>(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, cus, stream);
-  return w_stage_t<fp16>(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, cus, stream);
+  if (dtype == 1) return w_stage_t<fp16>(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, cus, stream);
+  // fp32: the fp32 GEMM writes the same split partials, reduced in the same order
+  hipError_t e = launch_w_stage32(p, x, dg, dfc, dw_g, dw_fc, M, K, N, ws, stream);
+  if (e != hipSuccess || p.splits == 1) return e;
+  int64_t blocks = ceil_div(K * 2 * N / 4, 256);
+  if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
+  hipLaunchKernelGGL((w_reduce_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, stream, ws,
+                     static_cast<float*>(dw_g), static_cast<float*>(dw_fc), K, N, p.splits);
+  return hipGetLastError();
 }
 
 template <typename T>

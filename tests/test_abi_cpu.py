@@ -139,10 +139,12 @@ def test_gemm_argument_errors(lib):
     assert lib.swiglu_bwd_w(*wa(M=0)) == OK
     assert lib.swiglu_bwd_w(*wa(K=0)) == OK
     assert lib.swiglu_bwd_w(*wa(M=-1)) == INVALID
-    assert lib.swiglu_bwd_w(*wa(dt=FP32)) == UNSUPPORTED
     assert lib.swiglu_bwd_w(*wa(dt=9)) == INVALID
-    assert lib.swiglu_bwd_w(*wa(K=60)) == UNSUPPORTED
+    assert lib.swiglu_bwd_w(*wa(K=60)) == UNSUPPORTED                 # 16-bit: multiples of 8
     assert lib.swiglu_bwd_w(*wa(N=100)) == UNSUPPORTED
+    assert lib.swiglu_bwd_w(*wa(dt=FP32, K=62)) == UNSUPPORTED        # fp32: multiples of 4
+    assert lib.swiglu_bwd_w(*wa(dt=FP32, N=102)) == UNSUPPORTED
+    assert lib.swiglu_bwd_w(*wa(dt=FP32, x=NULL)) == NULLPTR          # fp32 is a valid dtype
     for k in ("x", "dg", "dfc", "dwg", "dwfc"):
         assert lib.swiglu_bwd_w(*wa(**{k: NULL})) == NULLPTR, k
     if need > 0:
@@ -154,8 +156,9 @@ def test_gemm_argument_errors(lib):
     assert lib.swiglu_bwd_x(*xa(M=0)) == OK
     assert lib.swiglu_bwd_x(*xa(K=0, dx=NULL)) == OK
     assert lib.swiglu_bwd_x(*xa(K=-8)) == INVALID
-    assert lib.swiglu_bwd_x(*xa(dt=FP32)) == UNSUPPORTED
     assert lib.swiglu_bwd_x(*xa(N=12)) == UNSUPPORTED
+    assert lib.swiglu_bwd_x(*xa(dt=FP32, N=10)) == UNSUPPORTED
+    assert lib.swiglu_bwd_x(*xa(dt=FP32, dg=NULL)) == NULLPTR
     for k in ("dg", "dfc", "wg", "wfc", "dx"):
         assert lib.swiglu_bwd_x(*xa(**{k: NULL})) == NULLPTR, k
     assert lib.swiglu_bwd_x(*xa(N=0, dx=NULL)) == NULLPTR

@@ -109,7 +109,7 @@ def test_b_stage_unaligned_rows_use_scalar_path():
 
 
 @pytest.mark.parametrize("wl", ["tiny", "ragged"])
-@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
 def test_w_stage_workloads(wl, dt):
     inp = swiglu_inputs(wl, dtype=dt)
     dg, dfc = _oracle_dg(inp, dt)
@@ -125,7 +125,7 @@ def test_w_stage_accumulates_into_nonzero_dw():
 
 
 @pytest.mark.parametrize("wl", ["tiny", "ragged"])
-@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
 def test_x_stage_workloads(wl, dt):
     inp = swiglu_inputs(wl, dtype=dt)
     dg, dfc = _oracle_dg(inp, dt)
@@ -141,6 +141,25 @@ def test_gemm_stages_odd_shapes(M, K, N, dt):
     dg, dfc = _oracle_dg(inp, dt)
     _w_case(inp["x"], dg, dfc, dt)
     _x_case(dg, dfc, inp["w_g"], inp["w_fc"], dt)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4, 4), (63, 36, 132), (300, 260, 268), (129, 96, 196),
+                                   (700, 256, 128), (2000, 4, 1028), (513, 1028, 76)])
+def test_gemm_stages_fp32_odd_shapes(M, K, N):
+    """The fp32 path: K and N multiples of 4, partial tiles on every side, M split or not."""
+    inp = swiglu_inputs(SwiGLUShape("odd32", 14, M, K, N), dtype="fp32")
+    dg, dfc = _oracle_dg(inp, "fp32")
+    _w_case(inp["x"], dg, dfc, "fp32")
+    _x_case(dg, dfc, inp["w_g"], inp["w_fc"], "fp32")
+
+
+def test_w_stage_fp32_accumulates_into_nonzero_dw():
+    """Split partials (M = 8191) added to a non-zero fp32 dw."""
+    inp = swiglu_inputs("ragged", dtype="fp32")
+    dg, dfc = _oracle_dg(inp, "fp32")
+    K, N = inp["w_g"].shape
+    init = torch.linspace(-1.0, 1.0, K * N).reshape(K, N)
+    _w_case(inp["x"], dg, dfc, "fp32", dw0=init)
 
 
 def test_x_stage_empty_contraction_writes_zero():
