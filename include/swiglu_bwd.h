@@ -114,11 +114,11 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
  *   fc[m,n] = sum_k x[m,k] W_fc[k,n] + b_fc[n]
  *   y[m,n]  = SiLU(g[m,n]) * fc[m,n] = g sigma(g) fc
  * x: [M, K]; w_g, w_fc: [K, N]; b_g, b_fc: [N], or NULL for no bias; g, fc, y: [M, N],
- * OVERWRITTEN (g and fc are what swiglu_bwd_b takes).  dtype: bf16 or fp16 (fp32 returns
- * SWG_ERR_UNSUPPORTED); K and N multiples of 8 and below 2^22, M below 2^31, else
+ * OVERWRITTEN (g and fc are what swiglu_bwd_b takes).  dtype: bf16, fp16 or fp32; K and N
+ * multiples of 8 (bf16 / fp16) or of 4 (fp32) and below 2^22, M below 2^31, else
  * SWG_ERR_UNSUPPORTED.  Products on the matrix cores with fp32 accumulation; the bias is
  * added in fp32; y is formed from the fp32 values of g and fc (before their rounding); each
- * output is rounded once.  K = 0 gives g = b_g, fc = b_fc (the empty sums); x, w_g and
+ * output is rounded once (fp32: not rounded).  K = 0 gives g = b_g, fc = b_fc (the empty sums); x, w_g and
  * w_fc may then be NULL.  No aliasing between any two buffers.
  */
 swg_status swiglu_fwd(const void* x, const void* w_g, const void* w_fc,

@@ -286,14 +286,15 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
 swg_status swiglu_fwd(const void* x, const void* w_g, const void* w_fc, const void* b_g,
                       const void* b_fc, void* g, void* fc, void* y, int64_t M, int64_t K,
                       int64_t N, swg_dtype dtype, void* stream) {
-  swg_status st = gemm_shape_check(dtype, M, K, N);
+  swg_status st = gemm_shape_check(dtype, M, K, N, true);
   if (st != SWG_OK) return st;
   if (M == 0 || N == 0) return SWG_OK;  // outputs are empty
   if (!g || !fc || !y) return SWG_ERR_NULLPTR;
   if (K > 0 && (!x || !w_g || !w_fc)) return SWG_ERR_NULLPTR;
   for (const void* p : {x, w_g, w_fc, (const void*)g, (const void*)fc, (const void*)y})
     if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
-  for (const void* p : {b_g, b_fc}) if (!aligned(p, 2)) return SWG_ERR_INVALID;
+  for (const void* p : {b_g, b_fc})
+    if (!aligned(p, (size_t)elem_size(dtype))) return SWG_ERR_INVALID;
   return hip_status(launch_fwd(dtype, x, w_g, w_fc, b_g, b_fc, g, fc, y, M, K, N,
                                gemm_grid_cap(), as_stream(stream)));
 }

@@ -1378,7 +1378,8 @@ hipError_t launch_fwd(int dtype, const void* x, const void* w_g, const void* w_f
                       const void* b_g, const void* b_fc, void* g, void* fc, void* y, int64_t M,
                       int64_t K, int64_t N, int cus, hipStream_t stream) {
   if (dtype == 0) return fwd_t<bf16>(x, w_g, w_fc, b_g, b_fc, g, fc, y, M, K, N, cus, stream);
-  return fwd_t<fp16>(x, w_g, w_fc, b_g, b_fc, g, fc, y, M, K, N, cus, stream);
+  if (dtype == 1) return fwd_t<fp16>(x, w_g, w_fc, b_g, b_fc, g, fc, y, M, K, N, cus, stream);
+  return launch_fwd32(x, w_g, w_fc, b_g, b_fc, g, fc, y, M, K, N, stream);
 }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {

@@ -1,6 +1,7 @@
-// fp32 path of the w and x stages (fp32 tensors): the same two GEMMs as the bf16 / fp16
-// kernels [Fused SwiGLU backward page, formulas 3 and 4], on the fp32 matrix cores
-// (v_mfma_f32_32x32x2_f32), fp32 accumulation, one rounding-free store per output.
+// fp32 path of the w and x stages and of the SwiGLU forward (fp32 tensors): the same
+// GEMMs as the bf16 / fp16 kernels [Fused SwiGLU backward page, formulas 3 and 4; SwiGLU
+// page, operator background], on the fp32 matrix cores (v_mfma_f32_32x32x2_f32), fp32
+// accumulation, one rounding-free store per output.
 //
 // Output tiles of 128 x 128 per workgroup of four waves (2 x 2, each 64 x 64 = 2 x 2
 // blocks of 32 x 32 accumulators); the contraction advances 16 at a time through a
@@ -207,7 +208,63 @@ __global__ __launch_bounds__(NT32) void w_stage32_kernel(const float* __restrict
   }
 }
 
+// SwiGLU forward, fp32 [SwiGLU page, operator background]: g = x W_g + b_g,
+// fc = x W_fc + b_fc, y = g sigma(g) fc.  A = x rows m (contraction k contiguous);
+// B = W_g then W_fc, element (n, k) at W[k N + n] (rows n contiguous).  Biases may be
+// null (zero).
+__global__ __launch_bounds__(NT32) void fwd32_kernel(const float* __restrict__ x,
+                                                     const float* __restrict__ wg,
+                                                     const float* __restrict__ wfc,
+                                                     const float* __restrict__ bg,
+                                                     const float* __restrict__ bfc,
+                                                     float* __restrict__ g,
+                                                     float* __restrict__ fc,
+                                                     float* __restrict__ y, int64_t M,
+                                                     int64_t K, int64_t N, int64_t nn) {
+  __shared__ __attribute__((aligned(16))) float lds[4 * K32 * LD32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wp = wave >> 1, wq = wave & 1;
+  const int64_t m0 = (int64_t)(blockIdx.x / nn) * T32, n0 = (int64_t)(blockIdx.x % nn) * T32;
+  f32x16 ag[2][2], af[2][2];
+  zero32(ag);
+  zero32(af);
+  contract32<true, false>(x, K, m0, M, wg, N, n0, N, 0, K, lds, tid, wp, wq, lane, ag);
+  contract32<true, false>(x, K, m0, M, wfc, N, n0, N, 0, K, lds, tid, wp, wq, lane, af);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = wq * 64 + j * 32 + (lane & 31);
+      const int64_t n = n0 + col;
+      const float bgv = (bg != nullptr && n < N) ? bg[n] : 0.0f;
+      const float bfv = (bfc != nullptr && n < N) ? bfc[n] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wp * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m < M && n < N) {
+          const float gv = ag[i][j][r] + bgv, fv = af[i][j][r] + bfv;
+          const int64_t o = m * N + n;
+          g[o] = gv;
+          fc[o] = fv;
+          y[o] = gv * sigmoid_parts(gv).s * fv;
+        }
+      }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_fwd32(const void* x, const void* w_g, const void* w_fc, const void* b_g,
+                        const void* b_fc, void* g, void* fc, void* y, int64_t M, int64_t K,
+                        int64_t N, hipStream_t stream) {
+  const int64_t np = ceil_div(M, T32), nn = ceil_div(N, T32);
+  hipLaunchKernelGGL(fwd32_kernel, dim3((unsigned)(np * nn)), dim3(NT32), 0, stream,
+                     static_cast<const float*>(x), static_cast<const float*>(w_g),
+                     static_cast<const float*>(w_fc), static_cast<const float*>(b_g),
+                     static_cast<const float*>(b_fc), static_cast<float*>(g),
+                     static_cast<float*>(fc), static_cast<float*>(y), M, K, N, nn);
+  return hipGetLastError();
+}
 
 hipError_t launch_x_stage32(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
                             void* dx, int64_t M, int64_t K, int64_t N, hipStream_t stream) {

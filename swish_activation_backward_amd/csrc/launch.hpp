@@ -41,12 +41,15 @@ hipError_t launch_x_stage(int dtype, const void* dg, const void* dfc, const void
                           const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
                           hipStream_t stream);
 
-// fp32 tensors (dtype 2) of the two GEMM stages; called by launch_x_stage / launch_w_stage
+// fp32 tensors (dtype 2) of the GEMMs; called by launch_x_stage / launch_w_stage / launch_fwd
 hipError_t launch_x_stage32(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
                             void* dx, int64_t M, int64_t K, int64_t N, hipStream_t stream);
 hipError_t launch_w_stage32(const WPlan& p, const void* x, const void* dg, const void* dfc,
                             void* dw_g, void* dw_fc, int64_t M, int64_t K, int64_t N, float* ws,
                             hipStream_t stream);
+hipError_t launch_fwd32(const void* x, const void* w_g, const void* w_fc, const void* b_g,
+                        const void* b_fc, void* g, void* fc, void* y, int64_t M, int64_t K,
+                        int64_t N, hipStream_t stream);
 
 // SwiGLU forward: g, fc, y [M, N] from x [M, K], W_g, W_fc [K, N], b_g, b_fc [N] (may be
 // null); one persistent workgroup per CU.

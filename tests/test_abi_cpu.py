@@ -175,7 +175,9 @@ def test_forward_argument_errors(lib):
     assert lib.swiglu_fwd(*fa(M=0)) == OK
     assert lib.swiglu_fwd(*fa(N=0)) == OK
     assert lib.swiglu_fwd(*fa(M=-1)) == INVALID
-    assert lib.swiglu_fwd(*fa(dt=FP32)) == UNSUPPORTED
+    assert lib.swiglu_fwd(*fa(dt=FP32, K=36, g=NULL)) == NULLPTR   # fp32 accepted
+    assert lib.swiglu_fwd(*fa(dt=FP32, N=10)) == UNSUPPORTED        # K, N multiples of 4
+    assert lib.swiglu_fwd(*fa(dt=FP32, bg=ctypes.c_void_p(0x40002))) == INVALID
     assert lib.swiglu_fwd(*fa(dt=7)) == INVALID
     assert lib.swiglu_fwd(*fa(K=60)) == UNSUPPORTED
     assert lib.swiglu_fwd(*fa(N=100)) == UNSUPPORTED

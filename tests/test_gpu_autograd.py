@@ -71,3 +71,21 @@ def test_module_with_leading_dims_and_frozen_input():
     for name, p, r in zip(("dw_g", "dw_fc", "db_g", "db_fc"),
                           (mod.w_g, mod.w_fc, mod.b_g, mod.b_fc), ref[1:]):
         _close(name, p.grad, r)
+
+
+def test_autograd_fp32_end_to_end():
+    """fp32 parameters: forward, b, w and x in the fp32 kernels; no 16-bit rounding between
+    the stages, so the normwise agreement with float64 autograd is far tighter."""
+    dev = device()
+    inp = swiglu_inputs(SwiGLUShape("ag32", 22, 777, 132, 196), dtype="fp32")
+    x, w_g, w_fc, b_g, b_fc, dy = (inp[k] for k in ("x", "w_g", "w_fc", "b_g", "b_fc", "dy"))
+    ref_y, ref = _ref_grads(x, w_g, w_fc, b_g, b_fc, dy)
+    params = [t.to(dev).requires_grad_() for t in (x, w_g, w_fc, b_g, b_fc)]
+    note("autograd wrapper fp32")
+    y = swiglu(*params)
+    y.backward(dy.to(dev))
+    torch.cuda.synchronize()
+    _close("y", y, ref_y, rel=2.0 ** -16)
+    for name, p, r in zip(("dx", "dw_g", "dw_fc", "db_g", "db_fc"), params, ref):
+        _close(name, p.grad, r, rel=2.0 ** -16)
+

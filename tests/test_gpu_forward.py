@@ -64,7 +64,7 @@ def _fwd_case(inp, dt, bias=True, rows=None):
 
 
 @pytest.mark.parametrize("wl", ["tiny", "ragged"])
-@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
 def test_forward_workloads(wl, dt):
     _fwd_case(swiglu_inputs(wl, dtype=dt, with_forward=False), dt)
 
@@ -75,6 +75,12 @@ def test_forward_workloads(wl, dt):
 def test_forward_odd_shapes(M, K, N):
     inp = swiglu_inputs(SwiGLUShape("odd", 17, M, K, N), with_forward=False)
     _fwd_case(inp, "bf16")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4, 4), (63, 36, 132), (300, 260, 268), (257, 516, 12)])
+def test_forward_fp32_odd_shapes(M, K, N):
+    inp = swiglu_inputs(SwiGLUShape("odd32", 18, M, K, N), dtype="fp32", with_forward=False)
+    _fwd_case(inp, "fp32")
 
 
 def test_forward_without_bias():
