@@ -88,18 +88,22 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 __device__ inline uint32_t clamp_bytes(int64_t rows, int64_t row_bytes) {
   return rows > 0 ? (uint32_t)(rows * row_bytes) : 0u;
 }
-// 16 bytes per lane from `off` in window `r` to LDS at dst + OFS + 16 * lane (dst must be
-// wave-uniform).  Issued as inline asm: the loads' completion is tracked by the explicit
-// vmcnt waits of the pipeline (the compiler's own tracking of LDS-DMA stores would add
-// conservative waits that drain the ring).  The constant OFS is added to M0 inside the
-// asm so one scalar base serves all loads of a stage.
+// 16 bytes per lane from window `r` at soffset + voffset to LDS at dst + OFS + 16 * lane
+// (dst must be wave-uniform).  The hardware range check applies to voffset (plus the
+// instruction offset) against the window's size, not to soffset: a wave-uniform column or
+// stage offset can go into soffset while the per-lane row term in voffset keeps rows past
+// the window reading zeros.  Issued as inline asm: the loads' completion is tracked by
+// the explicit vmcnt waits of the pipeline (the compiler's own tracking of LDS-DMA stores
+// would add conservative waits that drain the ring).  The constant OFS is added to M0
+// inside the asm so one scalar base serves all loads of a stage.
 template <int OFS>
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint16_t* dst) {
+__device__ inline void dma16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                              const uint16_t* dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(LDS_AS const void*)dst);
-  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, %4 offen lds"
                :
-               : "v"(off), "s"(r), "s"(lds), "i"(OFS)
+               : "v"(voff), "s"(r), "s"(lds), "i"(OFS), "s"(soff)
                : "memory", "scc");   // s_add_u32 writes SCC
 }
 // Compiler-only fence: keeps LDS reads and writes on their side of a barrier without
@@ -256,42 +260,6 @@ __device__ inline void stage_mma(const FragSet<T>& f, f32x16 (&acc)[FP][FQ]) {
       for (int j = 0; j < FQ; ++j) acc[i][j] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j], acc[i][j]);
 }
 
-// One pipeline step u (0..3) of a ring round.  On entry the fragments of the stage in
-// slot u are in registers (set u % 2) and the three following stages are in flight.  The
-// step waits until this wave's loads of the stage in slot u + 1 have landed and its own
-// LDS reads are complete; the barrier then says that every wave's loads landed and that
-// every wave has finished reading slot u, which is refilled with the stage four ahead.
-// The MFMAs of the current stage run from registers while the next stage's fragments
-// are read from LDS into the other set.  Every issue is LOADS_PER_STAGE loads per wave,
-// always issued (stages past the end of the work load zeros), so "the stage in slot u + 1
-// has landed" is exactly "at most 2 stages of loads outstanding".
-#define SWG_PIPE_STEP(ISSUE_AHEAD, READ, frags, u)                        \
-  do {                                                                    \
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));            \
-    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                \
-    SWG_COMPILER_FENCE();                                                 \
-    __builtin_amdgcn_s_barrier();                                         \
-    SWG_COMPILER_FENCE();                                                 \
-    ISSUE_AHEAD(ring + (u) * SLOT);                                       \
-    READ(ring + (((u) + 1) & 3) * SLOT, frags[((u) + 1) & 1]);            \
-    stage_mma<T>(frags[(u) & 1], acc);                                    \
-    step_schedule<READS_PER_STEP>();                                      \
-  } while (0)
-
-// The last step of a tile: as SWG_PIPE_STEP with u = 3, but the next tile's first stage
-// (slot 0) is read only after the epilogue, so that no operand fragments are live while
-// the accumulators are written out.
-#define SWG_PIPE_LAST_STEP(ISSUE_AHEAD, frags)                            \
-  do {                                                                    \
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));            \
-    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                \
-    SWG_COMPILER_FENCE();                                                 \
-    __builtin_amdgcn_s_barrier();                                         \
-    SWG_COMPILER_FENCE();                                                 \
-    ISSUE_AHEAD(ring + 3 * SLOT);                                         \
-    stage_mma<T>(frags[1], acc);                                          \
-  } while (0)
-
 // Swap a value with the neighbouring lane (lane ^ 1): DPP quad_perm [1, 0, 3, 2].
 __device__ inline float swap_adjacent(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -398,42 +366,6 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
   }
 }
 
-// One tile's run of the ring: nst stages (a multiple of 4).  On entry the tile's first
-// stage has landed in slot 0 for every wave (the previous barrier says so); it is read
-// into fragment set 0 first.  The issue side runs four stages ahead and the LDS reads one
-// stage ahead, so the last four issues of a tile fetch the first stages of the next tile
-// (`nxt_ctx`); keeping that hand-over in a peeled last round leaves the steady-state
-// rounds free of branches.
-#define SWG_TILE_ROUNDS(ISSUE, READ, frags, cur_ctx, nxt_ctx, nst)                             \
-  do {                                                                                     \
-    int64_t t_ = 0;                                                                        \
-    READ(ring, frags[0]);                                                                  \
-    for (; t_ + 4 < (nst); t_ += 4) {                                                      \
-      SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 4, sl); }, READ, frags, 0);     \
-      SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 5, sl); }, READ, frags, 1);     \
-      SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 6, sl); }, READ, frags, 2);     \
-      SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(cur_ctx, t_ + 7, sl); }, READ, frags, 3);     \
-    }                                                                                      \
-    SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 0, sl); }, READ, frags, 0);            \
-    SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 1, sl); }, READ, frags, 1);            \
-    SWG_PIPE_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 2, sl); }, READ, frags, 2);            \
-    SWG_PIPE_LAST_STEP([&](uint16_t* sl) { ISSUE(nxt_ctx, 3, sl); }, frags);                \
-  } while (0)
-
-// Pipeline start: the first four stages of the first tile in flight, the first stage
-// landed for every wave.
-#define SWG_PIPE_PROLOGUE(ISSUE, ctx)                              \
-  do {                                                             \
-    ISSUE(ctx, 0, ring);                                           \
-    ISSUE(ctx, 1, ring + SLOT);                                    \
-    ISSUE(ctx, 2, ring + 2 * SLOT);                                \
-    ISSUE(ctx, 3, ring + 3 * SLOT);                                \
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * LOADS_PER_STAGE));     \
-    SWG_COMPILER_FENCE();                                          \
-    __builtin_amdgcn_s_barrier();                                  \
-    SWG_COMPILER_FENCE();                                          \
-  } while (0)
-
 // ----------------------------------------------------------------- x stage (NT)
 // A = [dg | dfc] rows p (M), B = [W_g | W_fc] rows q (K).  Double stage d < sD contracts
 // over columns 64 d .. of dg / W_g, d >= sD over the same columns of dfc / W_fc
@@ -537,18 +469,6 @@ __device__ inline uint32_t x_voff(const XIssue& is, const uint32_t (&aoff)[8], c
   return acol[i & 1] < is.lim ? aoff[i] : kOOB;
 }
 
-// dma16 with a wave-uniform byte offset in soffset (not range-checked: the window's rows
-// are checked through voffset alone)
-template <int OFS>
-__device__ inline void dma16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                              const uint16_t* dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(LDS_AS const void*)dst);
-  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, %4 offen lds"
-               :
-               : "v"(voff), "s"(r), "s"(lds), "i"(OFS), "s"(soff)
-               : "memory", "scc");
-}
 
 template <bool RAGGED>
 __device__ inline void x_issue_all(const XIssue& is, const uint32_t (&aoff)[8],
@@ -884,8 +804,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     aoff[i] += wp * 128;
   }
 #define W_READ(slot, f) w_read<T>((slot), aoff, boff, (f))
-  // one pipeline step u (0..3): as SWG_PIPE_STEP, with the stage's loads and the next
-  // stage's fragment reads spread between the MFMAs
+  // One pipeline step u (0..3) of a ring round.  On entry the fragments of the stage in
+  // slot u are in registers (set u % 2) and the three following stages are in flight.  The
+  // step waits until this wave's loads of the stage in slot u + 1 have landed and its own
+  // LDS reads are complete; the barrier then says that every wave's loads landed and that
+  // every wave has finished reading slot u, which is refilled with the stage four ahead
+  // (of the next item once the current one runs out).  The MFMAs of the current stage run
+  // from registers while the next stage's fragments are read from LDS into the other set;
+  // loads and reads are spread between the MFMAs (w_group).  Every issue is
+  // LOADS_PER_STAGE loads per wave, always issued (stages past the end of the work load
+  // zeros), so "the stage in slot u + 1 has landed" is exactly "at most 2 stages of loads
+  // outstanding".  The last step of an item reads nothing: the next item's first stage is
+  // read after the epilogue, so that no operand fragments are live while the accumulators
+  // are written out.
 #define W_STEP(ctx, st, u, READ_NEXT)                                                       \
   do {                                                                                    \
     __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));                            \
@@ -1193,7 +1124,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       boff[j] = row * FN + (((4 * (2 * wq + j) + q) ^ sw) << 3) + 4 * (sl & 1);
   }
 #define F_READ(slot, f) f_read<T>((slot), wp, lane, boff, (f))
-  // one pipeline step u (0..3), loads and next-stage reads spread between the MFMAs
+  // one pipeline step u (0..3), as the w stage's W_STEP
 #define F_STEP(ctx, st, u, READ_NEXT)                                                       \
   do {                                                                                    \
     __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));                            \
