@@ -175,10 +175,72 @@ __global__ __launch_bounds__(256) void swish_grad_strided_kernel(const T* grad, 
   }
 }
 
+// Two-dimensional views in which some tensor runs down the columns (stride 1 on the outer
+// dimension, e.g. a transposed matrix): element-at-a-time gathering would read or write
+// 2-byte elements a whole row apart.  Each workgroup takes a 64 x 64 tile of the logical
+// index space instead; each input is read along its own contiguous dimension into an LDS
+// tile (widened to fp32), and the output is written along its contiguous dimension, so
+// every global access of a wave covers consecutive addresses.
+constexpr int kTrTile = 64;
+
+template <typename T>
+__global__ __launch_bounds__(256) void swish_grad_tr2d_kernel(const T* grad, const T* x, T* out,
+                                                              int64_t R, int64_t C,
+                                                              int64_t sg0, int64_t sg1,
+                                                              int64_t sx0, int64_t sx1,
+                                                              int64_t so0, int64_t so1,
+                                                              float beta) {
+  __shared__ float tg[kTrTile][kTrTile + 1], tx[kTrTile][kTrTile + 1];
+  const int lo = threadIdx.x & 63, hi = threadIdx.x >> 6;   // 64 x 4 threads
+  const int64_t tc = (C + kTrTile - 1) / kTrTile;
+  const int64_t tiles = ((R + kTrTile - 1) / kTrTile) * tc;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t r0 = (t / tc) * kTrTile, c0 = (t % tc) * kTrTile;
+    // loads: along columns (lo -> c) for a row-contiguous tensor, else along rows
+#pragma unroll 4
+    for (int k = 0; k < kTrTile / 4; ++k) {
+      const int a = hi + 4 * k;
+      {
+        const bool down = sg1 != 1 && sg0 == 1;
+        const int rr = down ? lo : a, cc = down ? a : lo;
+        const int64_t r = r0 + rr, c = c0 + cc;
+        tg[rr][cc] = (r < R && c < C) ? to_f32(grad[r * sg0 + c * sg1]) : 0.0f;
+      }
+      {
+        const bool down = sx1 != 1 && sx0 == 1;
+        const int rr = down ? lo : a, cc = down ? a : lo;
+        const int64_t r = r0 + rr, c = c0 + cc;
+        tx[rr][cc] = (r < R && c < C) ? to_f32(x[r * sx0 + c * sx1]) : 0.0f;
+      }
+    }
+    __syncthreads();
+    const bool down = so1 != 1 && so0 == 1;
+#pragma unroll 4
+    for (int k = 0; k < kTrTile / 4; ++k) {
+      const int a = hi + 4 * k;
+      const int rr = down ? lo : a, cc = down ? a : lo;
+      const int64_t r = r0 + rr, c = c0 + cc;
+      if (r < R && c < C)
+        out[r * so0 + c * so1] = from_f32<T>(tg[rr][cc] * swish_factor(beta * tx[rr][cc]));
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T>
 static hipError_t swish_grad_strided_t(const void* grad, const void* x, void* out,
                                        const StridedView& v, int64_t n, float beta,
                                        hipStream_t stream) {
+  if (v.nd == 2 && (v.stride[0][0] == 1 || v.stride[1][0] == 1 || v.stride[2][0] == 1)) {
+    const int64_t R = v.size[0], C = v.size[1];
+    int64_t tiles = ceil_div(R, kTrTile) * ceil_div(C, kTrTile);
+    if (tiles > kMaxStreamBlocks) tiles = kMaxStreamBlocks;
+    hipLaunchKernelGGL((swish_grad_tr2d_kernel<T>), dim3((unsigned)tiles), dim3(256), 0, stream,
+                       static_cast<const T*>(grad), static_cast<const T*>(x),
+                       static_cast<T*>(out), R, C, v.stride[0][0], v.stride[0][1],
+                       v.stride[1][0], v.stride[1][1], v.stride[2][0], v.stride[2][1], beta);
+    return hipGetLastError();
+  }
   StridedArgs a;
   a.nd = v.nd;
   // 32-bit path: every index below 2^32 and every divisor at most 2^31 (the magic

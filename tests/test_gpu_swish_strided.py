@@ -155,9 +155,10 @@ def test_empty_views():
     assert out.shape == (5, 0)
 
 
-def test_more_than_2_32_elements():
-    """A broadcast view of 65537 x 65537 > 2^32 elements into an 8.6 GB output: the 64-bit
-    index path.  Sampled outputs (the first and last rows and columns included)."""
+def test_more_than_2_32_elements_2d():
+    """A broadcast view of 65537 x 65537 > 2^32 elements into an 8.6 GB output (the 2-D
+    tiled kernel, its tile loop past 2^20 tiles).  Sampled outputs (the first and last rows
+    and columns included)."""
     dev = device()
     gs, _ = _values("bf16", (65537,), 28)
     _, xs = _values("bf16", (65537,), 29)
@@ -176,3 +177,28 @@ def test_more_than_2_32_elements():
     gsel = gs[torch.from_numpy(cols)]
     xsel = xs[torch.from_numpy(rows)]
     _check("2^32+ broadcast", got, gsel, xsel, "bf16", 1.702)
+
+
+def test_more_than_2_32_elements_3d():
+    """2 x 65537 x 32769 > 2^32 elements that stay three dimensions after merging: the
+    gather kernel's 64-bit index path."""
+    dev = device()
+    R, C = 65537, 32769
+    gs, _ = _values("bf16", (C,), 30)
+    _, xs = _values("bf16", (R,), 31)
+    g = gs.to(dev).view(1, 1, C).expand(2, R, C)
+    x = xs.to(dev).view(1, R, 1).expand(2, R, C)
+    out = torch.empty(2, R, C, dtype=torch.bfloat16, device=dev)
+    note("strided swish: 2 x 65537 x 32769 broadcast (64-bit indices, 3-D)")
+    swg.swish_grad(g, x, grad_x=out, beta=0.9)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    b = np.concatenate([[0, 1, 1], rng.integers(0, 2, 4000)])
+    rows = np.concatenate([[0, R - 1, R - 1], rng.integers(0, R, 4000)])
+    cols = np.concatenate([[0, C - 1, 0], rng.integers(0, C, 4000)])
+    idx = [torch.from_numpy(v).to(dev) for v in (b, rows, cols)]
+    got = out[idx[0], idx[1], idx[2]].cpu()
+    del out
+    _check("2^32+ broadcast 3-D", got, gs[torch.from_numpy(cols)], xs[torch.from_numpy(rows)],
+           "bf16", 0.9)
+
