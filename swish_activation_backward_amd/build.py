@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libswiglu_bwd.so")
-SOURCES = ["api.cpp", "elementwise.hip", "gemm.hip", "gemm32.hip"]
+SOURCES = ["api.cpp", "elementwise.hip", "strided.hip", "gemm.hip", "gemm32.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 ops are switched off: the device code is written in plain fp32 and

@@ -102,183 +102,6 @@ hipError_t launch_swish_grad(int dtype, const void* grad, const void* x, void* o
   }
 }
 
-// ------------------------------------------------------------------ strided swish_grad
-// Non-contiguous tensors (the SwishGrad page's aclnn interface, sections 3.5 and 4.2:
-// non-contiguous inputs are accepted and the result is written back into a possibly
-// non-contiguous output).
-// Instead of copying the inputs to contiguous buffers and the result back, one kernel
-// walks the logical index space and gathers / scatters through each tensor's strides.
-//
-// Index decomposition: per dimension (innermost first) q = i / size, r = i - q size.  When
-// n < 2^32 the division is a multiply-high by a precomputed magic number (unsigned
-// division by an invariant integer, Granlund and Montgomery, PLDI 1994: for divisor d,
-// s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1, q = (mulhi(i, m) + i) >> s).
-struct FastDiv32 {
-  uint32_t d, m, s;
-};
-
-struct StridedArgs {
-  int nd;
-  FastDiv32 div[kMaxStridedDims];
-  int64_t size[kMaxStridedDims];
-  int64_t sg[kMaxStridedDims], sx[kMaxStridedDims], so[kMaxStridedDims];
-};
-
-static FastDiv32 make_fastdiv(uint32_t d) {
-  FastDiv32 f;
-  f.d = d;
-  uint32_t s = 0;
-  while (s < 32 && (uint64_t(1) << s) < d) ++s;
-  f.s = s;
-  f.m = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
-  return f;
-}
-
-__device__ inline uint32_t fastdiv(uint32_t i, const FastDiv32& f) {
-  const uint64_t t = ((uint64_t)i * f.m) >> 32;
-  return (uint32_t)((t + i) >> f.s);
-}
-
-template <typename T, bool WIDE>
-__global__ __launch_bounds__(256) void swish_grad_strided_kernel(const T* grad, const T* x,
-                                                                 T* out, StridedArgs a,
-                                                                 int64_t n, float beta) {
-  const int64_t step = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += step) {
-    int64_t og = 0, ox = 0, oo = 0;
-    if (WIDE) {
-      int64_t idx = i;
-#pragma unroll
-      for (int k = kMaxStridedDims - 1; k >= 0; --k) {
-        if (k < a.nd) {
-          const int64_t q = idx / a.size[k], r = idx - q * a.size[k];
-          og += r * a.sg[k];
-          ox += r * a.sx[k];
-          oo += r * a.so[k];
-          idx = q;
-        }
-      }
-    } else {
-      uint32_t idx = (uint32_t)i;
-#pragma unroll
-      for (int k = kMaxStridedDims - 1; k >= 0; --k) {
-        if (k < a.nd) {
-          const uint32_t q = fastdiv(idx, a.div[k]), r = idx - q * a.div[k].d;
-          og += (int64_t)r * a.sg[k];
-          ox += (int64_t)r * a.sx[k];
-          oo += (int64_t)r * a.so[k];
-          idx = q;
-        }
-      }
-    }
-    out[oo] = from_f32<T>(to_f32(grad[og]) * swish_factor(beta * to_f32(x[ox])));
-  }
-}
-
-// Two-dimensional views in which some tensor runs down the columns (stride 1 on the outer
-// dimension, e.g. a transposed matrix): element-at-a-time gathering would read or write
-// 2-byte elements a whole row apart.  Each workgroup takes a 64 x 64 tile of the logical
-// index space instead; each input is read along its own contiguous dimension into an LDS
-// tile (widened to fp32), and the output is written along its contiguous dimension, so
-// every global access of a wave covers consecutive addresses.
-constexpr int kTrTile = 64;
-
-template <typename T>
-__global__ __launch_bounds__(256) void swish_grad_tr2d_kernel(const T* grad, const T* x, T* out,
-                                                              int64_t R, int64_t C,
-                                                              int64_t sg0, int64_t sg1,
-                                                              int64_t sx0, int64_t sx1,
-                                                              int64_t so0, int64_t so1,
-                                                              float beta) {
-  __shared__ float tg[kTrTile][kTrTile + 1], tx[kTrTile][kTrTile + 1];
-  const int lo = threadIdx.x & 63, hi = threadIdx.x >> 6;   // 64 x 4 threads
-  const int64_t tc = (C + kTrTile - 1) / kTrTile;
-  const int64_t tiles = ((R + kTrTile - 1) / kTrTile) * tc;
-  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-    const int64_t r0 = (t / tc) * kTrTile, c0 = (t % tc) * kTrTile;
-    // loads: along columns (lo -> c) for a row-contiguous tensor, else along rows
-#pragma unroll 4
-    for (int k = 0; k < kTrTile / 4; ++k) {
-      const int a = hi + 4 * k;
-      {
-        const bool down = sg1 != 1 && sg0 == 1;
-        const int rr = down ? lo : a, cc = down ? a : lo;
-        const int64_t r = r0 + rr, c = c0 + cc;
-        tg[rr][cc] = (r < R && c < C) ? to_f32(grad[r * sg0 + c * sg1]) : 0.0f;
-      }
-      {
-        const bool down = sx1 != 1 && sx0 == 1;
-        const int rr = down ? lo : a, cc = down ? a : lo;
-        const int64_t r = r0 + rr, c = c0 + cc;
-        tx[rr][cc] = (r < R && c < C) ? to_f32(x[r * sx0 + c * sx1]) : 0.0f;
-      }
-    }
-    __syncthreads();
-    const bool down = so1 != 1 && so0 == 1;
-#pragma unroll 4
-    for (int k = 0; k < kTrTile / 4; ++k) {
-      const int a = hi + 4 * k;
-      const int rr = down ? lo : a, cc = down ? a : lo;
-      const int64_t r = r0 + rr, c = c0 + cc;
-      if (r < R && c < C)
-        out[r * so0 + c * so1] = from_f32<T>(tg[rr][cc] * swish_factor(beta * tx[rr][cc]));
-    }
-    __syncthreads();
-  }
-}
-
-template <typename T>
-static hipError_t swish_grad_strided_t(const void* grad, const void* x, void* out,
-                                       const StridedView& v, int64_t n, float beta,
-                                       hipStream_t stream) {
-  if (v.nd == 2 && (v.stride[0][0] == 1 || v.stride[1][0] == 1 || v.stride[2][0] == 1)) {
-    const int64_t R = v.size[0], C = v.size[1];
-    int64_t tiles = ceil_div(R, kTrTile) * ceil_div(C, kTrTile);
-    if (tiles > kMaxStreamBlocks) tiles = kMaxStreamBlocks;
-    hipLaunchKernelGGL((swish_grad_tr2d_kernel<T>), dim3((unsigned)tiles), dim3(256), 0, stream,
-                       static_cast<const T*>(grad), static_cast<const T*>(x),
-                       static_cast<T*>(out), R, C, v.stride[0][0], v.stride[0][1],
-                       v.stride[1][0], v.stride[1][1], v.stride[2][0], v.stride[2][1], beta);
-    return hipGetLastError();
-  }
-  StridedArgs a;
-  a.nd = v.nd;
-  // 32-bit path: every index below 2^32 and every divisor at most 2^31 (the magic
-  // number then fits in 32 bits)
-  bool narrow = n <= 0xFFFFFFFFll;
-  for (int k = 0; k < kMaxStridedDims; ++k) {
-    const bool used = k < v.nd;
-    narrow = narrow && (!used || v.size[k] <= (int64_t(1) << 31));
-    a.size[k] = used ? v.size[k] : 1;
-    a.div[k] = make_fastdiv(used && v.size[k] <= (int64_t(1) << 31) ? (uint32_t)v.size[k] : 1u);
-    a.sg[k] = used ? v.stride[0][k] : 0;
-    a.sx[k] = used ? v.stride[1][k] : 0;
-    a.so[k] = used ? v.stride[2][k] : 0;
-  }
-  int64_t blocks = ceil_div(n, 256);
-  if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
-  const T* g = static_cast<const T*>(grad);
-  const T* xx = static_cast<const T*>(x);
-  T* o = static_cast<T*>(out);
-  if (narrow)
-    hipLaunchKernelGGL((swish_grad_strided_kernel<T, false>), dim3((unsigned)blocks), dim3(256),
-                       0, stream, g, xx, o, a, n, beta);
-  else
-    hipLaunchKernelGGL((swish_grad_strided_kernel<T, true>), dim3((unsigned)blocks), dim3(256),
-                       0, stream, g, xx, o, a, n, beta);
-  return hipGetLastError();
-}
-
-hipError_t launch_swish_grad_strided(int dtype, const void* grad, const void* x, void* out,
-                                     const StridedView& v, int64_t n, float beta,
-                                     hipStream_t stream) {
-  switch (dtype) {
-    case 0: return swish_grad_strided_t<bf16>(grad, x, out, v, n, beta, stream);
-    case 1: return swish_grad_strided_t<fp16>(grad, x, out, v, n, beta, stream);
-    default: return swish_grad_strided_t<float>(grad, x, out, v, n, beta, stream);
-  }
-}
-
 // ------------------------------------------------------------------ b stage
 // Workgroup = 256 lanes laid out as TY rows x TX vector-columns (TX = 2^txlog2).
 // blockIdx.x picks the column strip; blockIdx.y is the walker, which takes the row units
