@@ -4,9 +4,9 @@
 // accumulation, one rounding-free store per output.
 //
 // Output tiles of 128 x 128 per workgroup of four waves (2 x 2, each 64 x 64 = 2 x 2
-// blocks of 32 x 32 accumulators); the contraction advances 16 at a time through a
+// blocks of 32 x 32 accumulators); the contraction advances 32 at a time through a
 // double-buffered LDS stage (operands loaded as 16-byte vectors into registers, written
-// to LDS as [16 contraction][128] so that each lane's MFMA operand is one 4-byte read
+// to LDS as [32 contraction][128] so that each lane's MFMA operand is one 4-byte read
 // from a row of 128 consecutive floats).  The next stage's global loads are issued before
 // the current stage's MFMAs and written to the other LDS buffer after them.
 //
@@ -25,24 +25,26 @@ namespace swg {
 namespace {
 
 constexpr int T32 = 128;            // output tile rows and columns
-constexpr int K32 = 16;             // contraction per stage
+constexpr int K32 = 32;             // contraction per stage
 constexpr int LD32 = T32 + 4;       // LDS row pitch in floats (rows 16 bytes apart in bank)
 constexpr int NT32 = 256;
 
-// Two 16-byte vectors per lane cover a [128 rows][16 contraction] operand tile.
+// Four 16-byte vectors per lane cover a [128 rows][32 contraction] operand tile.
 template <bool CK>
 struct Tile32 {
-  f32x4 v[2];
+  static constexpr int NV = K32 / 8;   // 16-byte vectors per lane
+  static constexpr int RV = K32 / 4;   // 16-byte vectors per row (contraction-contiguous)
+  f32x4 v[NV];
 
-  // rows [p0, p0 + 128) limited to plim, contraction [r0, r0 + 16) limited to rlim
+  // rows [p0, p0 + 128) limited to plim, contraction [r0, r0 + K32) limited to rlim
   __device__ void load(const float* src, int64_t ld, int64_t p0, int64_t r0, int64_t plim,
                        int64_t rlim, int tid) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NV; ++h) {
       int64_t p, r;
       if (CK) {
-        p = p0 + (tid >> 2) + 64 * h;
-        r = r0 + (tid & 3) * 4;
+        p = p0 + (tid / RV) + (256 / RV) * h;
+        r = r0 + (tid % RV) * 4;
       } else {
         r = r0 + (tid >> 5) + 8 * h;
         p = p0 + (tid & 31) * 4;
@@ -53,12 +55,12 @@ struct Tile32 {
     }
   }
 
-  // to LDS [16][LD32]: element (p, r) at r * LD32 + p
+  // to LDS [K32][LD32]: element (p, r) at r * LD32 + p
   __device__ void store(float* lds, int tid) const {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NV; ++h) {
       if (CK) {
-        const int p = (tid >> 2) + 64 * h, r = (tid & 3) * 4;
+        const int p = (tid / RV) + (256 / RV) * h, r = (tid % RV) * 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) lds[(r + e) * LD32 + p] = v[h][e];
       } else {
