@@ -88,21 +88,23 @@ def test_forward_without_bias():
               "bf16", bias=False)
 
 
-def test_forward_empty_contraction_gives_bias_terms():
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_forward_empty_contraction_gives_bias_terms(dt):
     dev = device()
     M, N = 40, 24
-    b_g = torch.linspace(-3, 3, N).to(torch.bfloat16)
-    b_fc = torch.linspace(2, -1, N).to(torch.bfloat16)
-    g, fc, y = (torch.full((M, N), 7.0, dtype=torch.bfloat16, device=dev) for _ in range(3))
-    e = torch.empty(M, 0, dtype=torch.bfloat16, device=dev)
-    w = torch.empty(0, N, dtype=torch.bfloat16, device=dev)
-    note("forward K=0")
+    tdt = DTYPES[dt]
+    b_g = torch.linspace(-3, 3, N).to(tdt)
+    b_fc = torch.linspace(2, -1, N).to(tdt)
+    g, fc, y = (torch.full((M, N), 7.0, dtype=tdt, device=dev) for _ in range(3))
+    e = torch.empty(M, 0, dtype=tdt, device=dev)
+    w = torch.empty(0, N, dtype=tdt, device=dev)
+    note(f"forward K=0 {dt}")
     swg.swiglu_fwd(e, w, w, b_g.to(dev), b_fc.to(dev), g, fc, y)
     torch.cuda.synchronize()
     bg, bf = to64(b_g), to64(b_fc)
     want_y = bg * _sig(bg) * bf
     for name, got, want in (("g", g, bg), ("fc", fc, bf), ("y", y, want_y)):
-        compare(name, got.cpu(), np.broadcast_to(want, (M, N)), "bf16",
+        compare(name, got.cpu(), np.broadcast_to(want, (M, N)), dt,
                 model_abs=np.broadcast_to(8.0 * U32 * np.abs(want), (M, N)))
 
 

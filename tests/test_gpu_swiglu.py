@@ -162,13 +162,15 @@ def test_w_stage_fp32_accumulates_into_nonzero_dw():
     _w_case(inp["x"], dg, dfc, "fp32", dw0=init)
 
 
-def test_x_stage_empty_contraction_writes_zero():
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_x_stage_empty_contraction_writes_zero(dt):
     dev = device()
     M, K = 33, 16
-    dx = torch.full((M, K), 3.0, dtype=torch.bfloat16, device=dev)
-    e = torch.empty(M, 0, dtype=torch.bfloat16, device=dev)
-    w = torch.empty(K, 0, dtype=torch.bfloat16, device=dev)
-    note("x stage N=0")
+    tdt = DTYPES[dt]
+    dx = torch.full((M, K), 3.0, dtype=tdt, device=dev)
+    e = torch.empty(M, 0, dtype=tdt, device=dev)
+    w = torch.empty(K, 0, dtype=tdt, device=dev)
+    note(f"x stage N=0 {dt}")
     swg.swiglu_bwd_x(e, e, w, w, dx)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dx).item() == 0
