@@ -83,6 +83,23 @@ def test_forward_fp32_odd_shapes(M, K, N):
     _fwd_case(inp, "fp32")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_forward_random_shapes(seed):
+    """Seeded random shapes, bf16 / fp16 / fp32 in turn (K, N multiples of 8 or 4)."""
+    dt = ("bf16", "fp16", "fp32")[seed % 3]
+    vec = 4 if dt == "fp32" else 8
+    rng = np.random.default_rng(2000 + seed)
+    M = int(rng.integers(1, 3000))
+    K = int(rng.integers(0, 1100 // vec + 1)) * vec
+    N = int(rng.integers(1, 1100 // vec + 1)) * vec
+    inp = swiglu_inputs(SwiGLUShape("frand", 80 + seed, M, max(K, vec), N), dtype=dt,
+                        with_forward=False)
+    if K == 0:
+        inp["x"] = inp["x"][:, :0]
+        inp["w_g"], inp["w_fc"] = inp["w_g"][:0], inp["w_fc"][:0]
+    _fwd_case(inp, dt, bias=seed % 4 != 3)
+
+
 def test_forward_without_bias():
     _fwd_case(swiglu_inputs(SwiGLUShape("nobias", 5, 777, 136, 264), with_forward=False),
               "bf16", bias=False)

@@ -153,6 +153,36 @@ def test_gemm_stages_fp32_odd_shapes(M, K, N):
     _x_case(dg, dfc, inp["w_g"], inp["w_fc"], "fp32")
 
 
+def _random_shape(seed, vec):
+    """A seeded shape with K, N multiples of `vec` (the 16-byte row rule), sizes spread
+    over several tiles and partial tiles on every side."""
+    rng = np.random.default_rng(1000 + seed)
+    M = int(rng.integers(1, 3000))
+    K = int(rng.integers(1, 1100 // vec + 1)) * vec
+    N = int(rng.integers(1, 1100 // vec + 1)) * vec
+    return M, K, N
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_gemm_stages_random_shapes(seed):
+    """Seeded random shapes (bf16 and fp16 alternately): w and x against the oracle."""
+    M, K, N = _random_shape(seed, 8)
+    dt = "bf16" if seed % 2 == 0 else "fp16"
+    inp = swiglu_inputs(SwiGLUShape("rand", 40 + seed, M, K, N), dtype=dt)
+    dg, dfc = _oracle_dg(inp, dt)
+    _w_case(inp["x"], dg, dfc, dt)
+    _x_case(dg, dfc, inp["w_g"], inp["w_fc"], dt)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gemm_stages_fp32_random_shapes(seed):
+    M, K, N = _random_shape(100 + seed, 4)
+    inp = swiglu_inputs(SwiGLUShape("rand32", 60 + seed, M, K, N), dtype="fp32")
+    dg, dfc = _oracle_dg(inp, "fp32")
+    _w_case(inp["x"], dg, dfc, "fp32")
+    _x_case(dg, dfc, inp["w_g"], inp["w_fc"], "fp32")
+
+
 def test_w_stage_fp32_accumulates_into_nonzero_dw():
     """Split partials (M = 8191) added to a non-zero fp32 dw."""
     inp = swiglu_inputs("ragged", dtype="fp32")
