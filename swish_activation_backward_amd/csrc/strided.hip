@@ -132,6 +132,104 @@ __global__ __launch_bounds__(256) void swish_grad_tr2d_kernel(const T* grad, con
   }
 }
 
+// The same tile with 4-element vectors: a lane moves 4 consecutive elements along its
+// tensor's contiguous dimension (8 bytes for 16-bit types, 16 for fp32), 16 lanes cover a
+// 64-element line of the tile, four passes the whole tile.  Used when every tensor's other
+// stride is a multiple of 4 and its pointer 4-element aligned; a vector that crosses the
+// edge of the view falls back to element accesses.
+template <typename T>
+struct Line4 {
+  typedef T V __attribute__((ext_vector_type(4)));
+  // direction 0: along columns (stride 1 on dimension 1), 1: along rows
+  __device__ static void load(const T* p, int64_t s0, int64_t s1, int dir, int64_t r, int64_t c,
+                              int64_t R, int64_t C, float (&v)[4]) {
+    const int64_t lim = dir == 0 ? C - c : R - r;   // elements left on the line
+    if (r < R && c < C && lim >= 4) {
+      const V t = *reinterpret_cast<const V*>(p + r * s0 + c * s1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = to_f32(t[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t rr = dir == 0 ? r : r + e, cc = dir == 0 ? c + e : c;
+        v[e] = (rr < R && cc < C) ? to_f32(p[rr * s0 + cc * s1]) : 0.0f;
+      }
+    }
+  }
+  __device__ static void store(T* p, int64_t s0, int64_t s1, int dir, int64_t r, int64_t c,
+                               int64_t R, int64_t C, const float (&v)[4]) {
+    const int64_t lim = dir == 0 ? C - c : R - r;
+    if (r < R && c < C && lim >= 4) {
+      V t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = from_f32<T>(v[e]);
+      *reinterpret_cast<V*>(p + r * s0 + c * s1) = t;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t rr = dir == 0 ? r : r + e, cc = dir == 0 ? c + e : c;
+        if (rr < R && cc < C) p[rr * s0 + cc * s1] = from_f32<T>(v[e]);
+      }
+    }
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void swish_grad_tr2d_vec_kernel(
+    const T* grad, const T* x, T* out, int64_t R, int64_t C, int64_t sg0, int64_t sg1,
+    int64_t sx0, int64_t sx1, int64_t so0, int64_t so1, float beta) {
+  __shared__ float tg[kTrTile][kTrTile + 1], tx[kTrTile][kTrTile + 1];
+  const int idx = threadIdx.x & 15, grp = threadIdx.x >> 4;   // 16 lanes per line
+  const int dg = (sg1 != 1 && sg0 == 1) ? 1 : 0;
+  const int dx = (sx1 != 1 && sx0 == 1) ? 1 : 0;
+  const int dout = (so1 != 1 && so0 == 1) ? 1 : 0;
+  const int64_t tc = (C + kTrTile - 1) / kTrTile;
+  const int64_t tiles = ((R + kTrTile - 1) / kTrTile) * tc;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t r0 = (t / tc) * kTrTile, c0 = (t % tc) * kTrTile;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int line = grp + 16 * pass, off = idx * 4;
+      float v[4];
+      {
+        const int rr = dg == 0 ? line : off, cc = dg == 0 ? off : line;
+        Line4<T>::load(grad, sg0, sg1, dg, r0 + rr, c0 + cc, R, C, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tg[dg == 0 ? rr : rr + e][dg == 0 ? cc + e : cc] = v[e];
+      }
+      {
+        const int rr = dx == 0 ? line : off, cc = dx == 0 ? off : line;
+        Line4<T>::load(x, sx0, sx1, dx, r0 + rr, c0 + cc, R, C, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tx[dx == 0 ? rr : rr + e][dx == 0 ? cc + e : cc] = v[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int line = grp + 16 * pass, off = idx * 4;
+      const int rr = dout == 0 ? line : off, cc = dout == 0 ? off : line;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ar = dout == 0 ? rr : rr + e, ac = dout == 0 ? cc + e : cc;
+        v[e] = tg[ar][ac] * swish_factor(beta * tx[ar][ac]);
+      }
+      Line4<T>::store(out, so0, so1, dout, r0 + rr, c0 + cc, R, C, v);
+    }
+    __syncthreads();
+  }
+}
+
+// Vector accesses are safe for a tensor when the stride of its other dimension is a
+// multiple of 4 and its pointer is aligned to 4 elements.
+static bool line4_ok(const void* p, int64_t s0, int64_t s1, int64_t es) {
+  const bool down = s1 != 1 && s0 == 1;
+  const int64_t other = down ? s1 : s0;
+  if (!down && s1 != 1) return false;   // neither dimension contiguous
+  return other % 4 == 0 && (reinterpret_cast<uintptr_t>(p) % (uintptr_t)(4 * es)) == 0;
+}
+
 template <typename T>
 static hipError_t swish_grad_strided_t(const void* grad, const void* x, void* out,
                                        const StridedView& v, int64_t n, float beta,
@@ -140,6 +238,16 @@ static hipError_t swish_grad_strided_t(const void* grad, const void* x, void* ou
     const int64_t R = v.size[0], C = v.size[1];
     int64_t tiles = ceil_div(R, kTrTile) * ceil_div(C, kTrTile);
     if (tiles > kMaxStreamBlocks) tiles = kMaxStreamBlocks;
+    const int64_t es = (int64_t)sizeof(T);
+    if (line4_ok(grad, v.stride[0][0], v.stride[0][1], es) &&
+        line4_ok(x, v.stride[1][0], v.stride[1][1], es) &&
+        line4_ok(out, v.stride[2][0], v.stride[2][1], es)) {
+      hipLaunchKernelGGL((swish_grad_tr2d_vec_kernel<T>), dim3((unsigned)tiles), dim3(256), 0,
+                         stream, static_cast<const T*>(grad), static_cast<const T*>(x),
+                         static_cast<T*>(out), R, C, v.stride[0][0], v.stride[0][1],
+                         v.stride[1][0], v.stride[1][1], v.stride[2][0], v.stride[2][1], beta);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((swish_grad_tr2d_kernel<T>), dim3((unsigned)tiles), dim3(256), 0, stream,
                        static_cast<const T*>(grad), static_cast<const T*>(x),
                        static_cast<T*>(out), R, C, v.stride[0][0], v.stride[0][1],

@@ -48,6 +48,36 @@ def test_transposed_inputs(dt, beta):
     _check("transposed", out, g, x, dt, beta)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+def test_transposed_with_aligned_strides(dt):
+    """Strides that are multiples of 4: the 4-element-vector tile kernel, with partial
+    tiles on both edges."""
+    dev = device()
+    G, X = _values(dt, (1028, 516), 31)
+    g, x = G.to(dev).t(), X.to(dev).t()          # [516, 1028], strides (1, 516)
+    note(f"strided swish: transposed, aligned strides {dt}")
+    out = swg.swish_grad(g, x, beta=1.702)
+    torch.cuda.synchronize()
+    _check("transposed aligned", out, g, x, dt, 1.702)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_transposed_partial_vectors(dt):
+    """Rows and columns that are not multiples of 4 (vectors cut by the edge fall back to
+    elements); the output's padding columns must stay untouched."""
+    dev = device()
+    G, X = _values(dt, (1026, 516), 32)
+    g = G.to(dev)[:, :515].t()                   # [515, 1026], strides (1, 516)
+    x = X.to(dev)[:, :515].t()
+    base = torch.full((515, 1028), float("nan"), dtype=DTYPES[dt], device=dev)
+    out = base[:, :1026]                         # strides (1028, 1)
+    note(f"strided swish: partial vectors {dt}")
+    swg.swish_grad(g, x, grad_x=out, beta=-0.5)
+    torch.cuda.synchronize()
+    assert torch.isnan(base[:, 1026:]).all(), "the kernel wrote past the view"
+    _check("partial vectors", out, g, x, dt, -0.5)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
 def test_sliced_with_step_and_gapped_output(dt):
     """Inputs sliced with a step of 2; the output is every other column of a buffer whose
