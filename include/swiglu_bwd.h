@@ -83,7 +83,8 @@ size_t swiglu_bwd_b_workspace_size(int64_t M, int64_t N, swg_dtype dtype);
  *   dw_fc[k,n] = RNE(dw_fc[k,n] + sum_m x[m,k] * dfc[m,n])
  * x: [M, K]; dg, dfc: [M, N]; dw_g, dw_fc: [K, N].  dtype: bf16, fp16 or fp32.  K and N
  * must be multiples of 8 (bf16 / fp16) or of 4 (fp32), i.e. 16-byte rows, and below 2^22,
- * and M below 2^31, otherwise SWG_ERR_UNSUPPORTED.  Products are formed on the matrix
+ * and M below 2^31; x, dg and dfc must be 16-byte aligned and dw_g, dw_fc 8-byte aligned;
+ * otherwise SWG_ERR_UNSUPPORTED.  Products are formed on the matrix
  * cores, accumulated in fp32 (split over M in fixed-order fp32 partials when the output is
  * small), added to the current dw and rounded once (fp32: not rounded): dw is ACCUMULATED
  * like db.  `workspace` holds swiglu_bwd_w_workspace_size(M, K, N, dtype) bytes (0 when
@@ -100,7 +101,7 @@ size_t swiglu_bwd_w_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dt
  * one GEMM [M, 2N] x [2N, K]:  dx[m,k] = sum_n dg[m,n] W_g[k,n] + dfc[m,n] W_fc[k,n].
  * dg, dfc: [M, N]; w_g, w_fc: [K, N] (row-major, as on the page); dx: [M, K], OVERWRITTEN.
  * dtype: bf16, fp16 or fp32; K and N multiples of 8 (bf16 / fp16) or of 4 (fp32) and
- * below 2^22, M below 2^31 (else SWG_ERR_UNSUPPORTED).  fp32 accumulation, one rounding
+ * below 2^22, M below 2^31, every pointer 16-byte aligned (else SWG_ERR_UNSUPPORTED).  fp32 accumulation, one rounding
  * (none for fp32).  N = 0 with M*K > 0 writes dx = 0 (the empty sum).
  */
 swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
@@ -115,8 +116,9 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
  *   y[m,n]  = SiLU(g[m,n]) * fc[m,n] = g sigma(g) fc
  * x: [M, K]; w_g, w_fc: [K, N]; b_g, b_fc: [N], or NULL for no bias; g, fc, y: [M, N],
  * OVERWRITTEN (g and fc are what swiglu_bwd_b takes).  dtype: bf16, fp16 or fp32; K and N
- * multiples of 8 (bf16 / fp16) or of 4 (fp32) and below 2^22, M below 2^31, else
- * SWG_ERR_UNSUPPORTED.  Products on the matrix cores with fp32 accumulation; the bias is
+ * multiples of 8 (bf16 / fp16) or of 4 (fp32) and below 2^22, M below 2^31, and x, w_g,
+ * w_fc, g, fc, y 16-byte aligned, else SWG_ERR_UNSUPPORTED (a bias that is not aligned to
+ * its element size: SWG_ERR_INVALID).  Products on the matrix cores with fp32 accumulation; the bias is
  * added in fp32; y is formed from the fp32 values of g and fc (before their rounding); each
  * output is rounded once (fp32: not rounded).  K = 0 gives g = b_g, fc = b_fc (the empty sums); x, w_g and
  * w_fc may then be NULL.  No aliasing between any two buffers.
@@ -147,7 +149,7 @@ swg_status swish_grad(const void* grad, const void* x, void* grad_x, int64_t n,
  * logical index (0, ..., 0).  Dimensions that are contiguous in all three tensors are
  * merged first; a view that is contiguous after merging runs the contiguous kernel.
  * Errors: SWG_ERR_INVALID for a negative size, an element count that overflows int64,
- * misaligned pointers, an output whose elements overlap each other, or an output that
+ * a view whose byte span overflows int64 (or a stride of INT64_MIN), misaligned pointers, an output whose elements overlap each other, or an output that
  * overlaps an input other than as the exact same view (same pointer and strides, which
  * is in-place); SWG_ERR_UNSUPPORTED when more than 8 dimensions remain after merging.
  * Empty views (a size of 0) return SWG_OK without touching the pointers.

@@ -114,6 +114,18 @@ swg_status swish_grad_strided(const void* grad, const void* x, void* grad_x, int
   if (!aligned(grad, (size_t)es) || !aligned(x, (size_t)es) || !aligned(grad_x, (size_t)es))
     return SWG_ERR_INVALID;
   const int64_t* st[3] = {grad_strides, x_strides, out_strides};
+  // every view's byte span must be representable: |stride| and (size - 1) * stride * es
+  // for each dimension, and their sums, without int64 overflow
+  for (int t = 0; t < 3; ++t) {
+    int64_t lo = 0, hi = 0;
+    for (int d = 0; d < ndim; ++d) {
+      int64_t e;
+      if (st[t][d] == INT64_MIN || __builtin_mul_overflow(sizes[d] - 1, st[t][d], &e) ||
+          __builtin_mul_overflow(e, es, &e) ||
+          __builtin_add_overflow(e < 0 ? lo : hi, e, e < 0 ? &lo : &hi))
+        return SWG_ERR_INVALID;
+    }
+  }
 
   // the output's elements must not overlap each other: with its dimensions of size > 1
   // sorted by |stride|, each stride must exceed the extent spanned by the smaller ones
@@ -146,20 +158,20 @@ swg_status swish_grad_strided(const void* grad, const void* x, void* grad_x, int
   }
   // byte span [lo, hi] of each view; the output may meet an input only as the same view
   {
-    auto span = [&](const void* p, const int64_t* s, intptr_t& lo, intptr_t& hi) {
-      int64_t a = 0, b = 0;
+    auto span = [&](const void* p, const int64_t* s, __int128& lo, __int128& hi) {
+      int64_t a = 0, b = 0;   // no overflow: checked above
       for (int d = 0; d < ndim; ++d) {
-        const int64_t e = (sizes[d] - 1) * s[d];
+        const int64_t e = (sizes[d] - 1) * s[d] * es;
         if (e < 0) a += e; else b += e;
       }
-      lo = reinterpret_cast<intptr_t>(p) + (intptr_t)(a * es);
-      hi = reinterpret_cast<intptr_t>(p) + (intptr_t)(b * es) + (intptr_t)es - 1;
+      lo = (__int128)reinterpret_cast<uintptr_t>(p) + a;
+      hi = (__int128)reinterpret_cast<uintptr_t>(p) + b + es - 1;
     };
-    intptr_t olo, ohi;
+    __int128 olo, ohi;
     span(grad_x, out_strides, olo, ohi);
     const void* ins[2] = {grad, x};
     for (int t = 0; t < 2; ++t) {
-      intptr_t lo, hi;
+      __int128 lo, hi;
       span(ins[t], st[t], lo, hi);
       if (lo > ohi || olo > hi) continue;   // disjoint
       bool same = ins[t] == grad_x;

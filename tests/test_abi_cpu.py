@@ -99,6 +99,15 @@ def test_swish_grad_strided_argument_errors(lib):
     assert f(P, Q, ctypes.c_void_p(0x10000 + 4), 2, _i64(3, 4), c2, c2, c2, BF16, beta,
              NULL) == INVALID
     assert f(P, Q, P, 2, _i64(3, 4), _i64(1, 3), c2, c2, BF16, beta, NULL) == INVALID
+    # strides whose byte span does not fit int64 (input or output), and INT64_MIN
+    huge = _i64(1 << 62, 1)
+    assert f(P, Q, R, 2, _i64(3, 4), huge, c2, c2, BF16, beta, NULL) == INVALID
+    assert f(P, Q, R, 2, _i64(3, 4), c2, huge, c2, BF16, beta, NULL) == INVALID
+    assert f(P, Q, R, 2, _i64(3, 4), c2, c2, huge, BF16, beta, NULL) == INVALID
+    assert f(P, Q, R, 2, _i64(3, 4), _i64(-(1 << 63), 1), c2, c2, BF16, beta,
+             NULL) == INVALID
+    assert f(P, Q, R, 2, _i64(1, 4), c2, c2, _i64(-(1 << 63), 1), BF16, beta,
+             NULL) == INVALID
     # nine dimensions that cannot be merged (x runs the other way round)
     sizes = _i64(*([2] * 9))
     rowmajor = _i64(*[1 << (8 - d) for d in range(9)])
