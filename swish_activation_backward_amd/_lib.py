@@ -94,9 +94,20 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _on_device(device):
+    """Context that makes ``device`` HIP's current device for the launch (the library
+    launches on the current device); host tensors are refused."""
+    if device.type != "cuda":
+        raise ValueError(f"tensor on {device}: the library computes on the GPU only "
+                         f"(move inputs and outputs to a cuda device)")
+    return torch.cuda.device(device)
+
+
+def _stream(stream, device):
+    """The stream handle to launch on: ``stream``, else torch's current stream of the
+    tensors' device."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -124,13 +135,21 @@ def _dtype_code(t):
     return DTYPE_CODE[t.dtype]
 
 
-def _workspace(nbytes, workspace, device):
+def _workspace(nbytes, workspace, device, stream):
+    """The caller's workspace (checked), or a new one from torch's allocator.  A new one is
+    marked as used on ``stream`` so that the allocator does not hand its memory out again
+    before the kernels queued there have finished with it."""
     if nbytes == 0:
         return workspace
     if workspace is None:
-        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if stream is not None:
+            ws.record_stream(stream)
+        return ws
     if workspace.numel() * workspace.element_size() < nbytes or not workspace.is_contiguous():
         raise ValueError(f"workspace needs {nbytes} contiguous bytes")
+    if workspace.device != device:
+        raise ValueError(f"workspace is on {workspace.device}, expected {device}")
     return workspace
 
 
@@ -163,8 +182,9 @@ def swish_grad(grad, x, grad_x=None, beta=None, stream=None):
         return swish_grad_strided(grad, x, grad_x, beta=beta, stream=stream)
     lib = load_library()
     b = None if beta is None else ctypes.byref(ctypes.c_float(beta))
-    st = lib.swish_grad(_ptr(grad), _ptr(x), _ptr(grad_x), grad.numel(), _dtype_code(grad), b,
-                        _stream(stream))
+    with _on_device(grad.device):
+        st = lib.swish_grad(_ptr(grad), _ptr(x), _ptr(grad_x), grad.numel(), _dtype_code(grad),
+                            b, _stream(stream, grad.device))
     _check("swish_grad", st, lib)
     return grad_x
 
@@ -180,8 +200,9 @@ def swish_grad_strided(grad, x, grad_x, beta=None, stream=None):
     sizes = arr(*grad.shape)
     sg, sx, so = arr(*grad.stride()), arr(*x.stride()), arr(*grad_x.stride())
     b = None if beta is None else ctypes.byref(ctypes.c_float(beta))
-    st = lib.swish_grad_strided(_ptr(grad), _ptr(x), _ptr(grad_x), nd, sizes, sg, sx, so,
-                                _dtype_code(grad), b, _stream(stream))
+    with _on_device(grad.device):
+        st = lib.swish_grad_strided(_ptr(grad), _ptr(x), _ptr(grad_x), nd, sizes, sg, sx, so,
+                                    _dtype_code(grad), b, _stream(stream, grad.device))
     _check("swish_grad_strided", st, lib)
     return grad_x
 
@@ -209,10 +230,11 @@ def swiglu_bwd_b(dy, g, fc, dg, dfc, db_g, db_fc, workspace=None, stream=None):
         _dense(name, t, dt, t.shape, dev)
     code = _dtype_code(dy)
     nbytes = int(lib.swiglu_bwd_b_workspace_size(M, N, code))
-    ws = _workspace(nbytes, workspace, dev)
-    st = lib.swiglu_bwd_b(_ptr(dy), _ptr(g), _ptr(fc), _ptr(dg), _ptr(dfc), _ptr(db_g),
-                          _ptr(db_fc), M, N, code, _ptr(ws), 0 if ws is None else
-                          ws.numel() * ws.element_size(), _stream(stream))
+    with _on_device(dev):
+        ws = _workspace(nbytes, workspace, dev, stream)
+        st = lib.swiglu_bwd_b(_ptr(dy), _ptr(g), _ptr(fc), _ptr(dg), _ptr(dfc), _ptr(db_g),
+                              _ptr(db_fc), M, N, code, _ptr(ws), 0 if ws is None else
+                              ws.numel() * ws.element_size(), _stream(stream, dev))
     _check("swiglu_bwd_b", st, lib)
 
 
@@ -231,10 +253,11 @@ def swiglu_bwd_w(x, dg, dfc, dw_g, dw_fc, workspace=None, stream=None):
         _dense(name, t, dt, (K, N), dev)
     code = _dtype_code(x)
     nbytes = int(lib.swiglu_bwd_w_workspace_size(M, K, N, code))
-    ws = _workspace(nbytes, workspace, dev)
-    st = lib.swiglu_bwd_w(_ptr(x), _ptr(dg), _ptr(dfc), _ptr(dw_g), _ptr(dw_fc), M, K, N, code,
-                          _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                          _stream(stream))
+    with _on_device(dev):
+        ws = _workspace(nbytes, workspace, dev, stream)
+        st = lib.swiglu_bwd_w(_ptr(x), _ptr(dg), _ptr(dfc), _ptr(dw_g), _ptr(dw_fc), M, K, N,
+                              code, _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(stream, dev))
     _check("swiglu_bwd_w", st, lib)
 
 
@@ -246,12 +269,14 @@ def swiglu_bwd_x(dg, dfc, w_g, w_fc, dx, stream=None):
     M, N = dg.shape
     K = w_g.shape[0]
     dt, dev = dg.dtype, dg.device
-    _dense("dfc", dfc, dt, (M, N), dev)
+    for name, t in (("dg", dg), ("dfc", dfc)):
+        _dense(name, t, dt, (M, N), dev)
     for name, t in (("w_g", w_g), ("w_fc", w_fc)):
         _dense(name, t, dt, (K, N), dev)
     _dense("dx", dx, dt, (M, K), dev)
-    st = lib.swiglu_bwd_x(_ptr(dg), _ptr(dfc), _ptr(w_g), _ptr(w_fc), _ptr(dx), M, K, N,
-                          _dtype_code(dg), _stream(stream))
+    with _on_device(dev):
+        st = lib.swiglu_bwd_x(_ptr(dg), _ptr(dfc), _ptr(w_g), _ptr(w_fc), _ptr(dx), M, K, N,
+                              _dtype_code(dg), _stream(stream, dev))
     _check("swiglu_bwd_x", st, lib)
 
 
@@ -264,6 +289,7 @@ def swiglu_fwd(x, w_g, w_fc, b_g, b_fc, g, fc, y, stream=None):
     M, K = x.shape
     N = w_g.shape[1]
     dt, dev = x.dtype, x.device
+    _dense("x", x, dt, (M, K), dev)
     for name, t in (("w_g", w_g), ("w_fc", w_fc)):
         _dense(name, t, dt, (K, N), dev)
     for name, t in (("b_g", b_g), ("b_fc", b_fc)):
@@ -271,6 +297,7 @@ def swiglu_fwd(x, w_g, w_fc, b_g, b_fc, g, fc, y, stream=None):
             _dense(name, t, dt, (N,), dev)
     for name, t in (("g", g), ("fc", fc), ("y", y)):
         _dense(name, t, dt, (M, N), dev)
-    st = lib.swiglu_fwd(_ptr(x), _ptr(w_g), _ptr(w_fc), _ptr(b_g), _ptr(b_fc), _ptr(g),
-                        _ptr(fc), _ptr(y), M, K, N, _dtype_code(x), _stream(stream))
+    with _on_device(dev):
+        st = lib.swiglu_fwd(_ptr(x), _ptr(w_g), _ptr(w_fc), _ptr(b_g), _ptr(b_fc), _ptr(g),
+                            _ptr(fc), _ptr(y), M, K, N, _dtype_code(x), _stream(stream, dev))
     _check("swiglu_fwd", st, lib)

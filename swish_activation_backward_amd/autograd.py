@@ -21,7 +21,7 @@ from . import _lib
 
 
 class SwiGLUFunction(torch.autograd.Function):
-    """x [M, K], w_g / w_fc [K, N], b_g / b_fc [N] or None -> y [M, N] (bf16 or fp16,
+    """x [M, K], w_g / w_fc [K, N], b_g / b_fc [N] or None -> y [M, N] (bf16, fp16 or fp32,
     contiguous, on the GPU)."""
 
     @staticmethod

@@ -241,3 +241,19 @@ def test_product_path_has_no_cpu_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("the oracle", ""), f
                 assert "numpy" not in text, f
+
+
+def test_binding_checks_every_operand_layout():
+    """Each operand's layout is checked, also the ones whose shape defines the sizes (x
+    of the forward, dg of the x stage): a transposed view is refused, not read as if it
+    were row-major."""
+    import torch
+    xt = torch.zeros(8, 4, dtype=torch.bfloat16).t()          # [4, 8], not contiguous
+    w = torch.zeros(8, 8, dtype=torch.bfloat16)
+    o = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="contiguous"):
+        swg.swiglu_fwd(xt, w, w, None, None, o, o.clone(), o.clone())
+    with pytest.raises(ValueError, match="contiguous"):
+        swg.swiglu_bwd_x(xt, o, w, w, torch.zeros(4, 8, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="dtype"):
+        swg.swiglu_fwd(o.half(), w, w, None, None, o, o.clone(), o.clone())
