@@ -115,6 +115,45 @@ def time_forward(swg, d, M, K, N, warmup, steps):
             "note": "SwiGLU forward (g, fc, y), timed separately; not part of the step"}
 
 
+def time_swish_context(swg, steps):
+    """The Swish gradient on the one workload the pages time: an fp16 [32, 64, 56, 56]
+    activation with beta = 1 (Ascend C custom-operator page, performance table).  Each
+    call is preceded by a 1 GiB write, so its inputs come from HBM and not from the
+    256 MB last-level cache; each call is bracketed by its own events.  Reported beside
+    the step, not part of `value`."""
+    import torch
+    from workloads.gen import SWISH_CONTEXT, swish_inputs
+    c = SWISH_CONTEXT
+    L = 1
+    for s in c["shape"]:
+        L *= s
+    dev = torch.device("cuda", 0)
+    inp = {k: v.reshape(c["shape"]).to(dev) for k, v in
+           swish_inputs(c["dtype"], L=L, seed=c["seed"]).items()}
+    out = torch.empty_like(inp["grad"])
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    times = []
+    for i in range(steps + 3):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        swg.swish_grad(inp["grad"], inp["x"], grad_x=out, beta=c["beta"])
+        e1.record(stream)
+        e1.synchronize()
+        if i >= 3:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    times.sort()
+    t = times[len(times) // 2]
+    nbytes = 3 * 2 * L
+    return {"shape": list(c["shape"]), "dtype": c["dtype"], "beta": c["beta"],
+            "median_us": round(t * 1e6, 2), "min_us": round(times[0] * 1e6, 2),
+            "GB/s": round(nbytes / t / 1e9, 1), "frac": round(nbytes / HBM_PEAK / t, 4),
+            "pages_us": {"ascend_c_kernel": 280, "autodiff": 420},
+            "note": "median of per-call events (launch overhead included) after a 1 GiB "
+                    "cache-evicting write; the pages' times are Ascend 910B, context only"}
+
+
 def copy_calibration(nbytes, reps=5):
     """A plain device-to-device copy of `nbytes`, for scaling the HBM byte counters."""
     import torch
@@ -322,6 +361,7 @@ def main():
         "roofline": roof,
     }
     out["forward"] = time_forward(swg, d, M, K, N, args.warmup, args.steps)
+    out["swish_pages_shape"] = time_swish_context(swg, 20)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, sw_inputs, args.cpu_rows, args.cpu_swish_len)
     print(json.dumps(out), flush=True)

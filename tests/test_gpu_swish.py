@@ -9,7 +9,7 @@ import oracle.ref as R
 import swish_activation_backward_amd as swg
 from gpu_util import Guarded, device, note
 from parity import TORCH_NAME, compare, swish_abs_model
-from workloads.gen import DTYPES, SWISH_WORKLOAD, swish_inputs
+from workloads.gen import DTYPES, SWISH_CONTEXT, SWISH_WORKLOAD, swish_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,24 @@ def test_swish_grad_full_length(dt, beta):
     ref = R.swish_grad_ref(grad.double().numpy(), x.double().numpy(), beta)
     compare(f"swish_grad[{dt},{beta}]", gx.cpu(), ref, dt,
             model_abs=swish_abs_model(grad.double().numpy(), x.double().numpy(), beta))
+
+
+def test_swish_grad_pages_timed_shape():
+    """The fp16 [32, 64, 56, 56] activation the Ascend C page times (beta = 1, SiLU
+    backward), as a 4-D contiguous tensor; every element compared."""
+    dev = device()
+    c = SWISH_CONTEXT
+    L = int(np.prod(c["shape"]))
+    inp = swish_inputs(c["dtype"], L=L, seed=c["seed"])
+    grad, x = inp["grad"].reshape(c["shape"]), inp["x"].reshape(c["shape"])
+    note(f"swish_grad {c['shape']} {c['dtype']} beta={c['beta']}")
+    gx = swg.swish_grad(grad.to(dev), x.to(dev), beta=c["beta"])
+    torch.cuda.synchronize()
+    assert gx.shape == grad.shape
+    g64, x64 = grad.reshape(-1).double().numpy(), x.reshape(-1).double().numpy()
+    ref = R.swish_grad_ref(g64, x64, c["beta"])
+    compare("swish_grad[32,64,56,56]", gx.reshape(-1).cpu(), ref, c["dtype"],
+            model_abs=swish_abs_model(g64, x64, c["beta"]))
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])

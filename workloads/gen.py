@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = [
-    "SwiGLUShape", "SWIGLU_WORKLOADS", "SWISH_WORKLOAD", "swiglu_inputs",
+    "SwiGLUShape", "SWIGLU_WORKLOADS", "SWISH_WORKLOAD", "SWISH_CONTEXT", "swiglu_inputs",
     "swish_inputs", "sha256_of", "DTYPES",
 ]
 
@@ -57,6 +57,12 @@ SWIGLU_WORKLOADS = {
 # three storage dtypes and three beta values.
 SWISH_WORKLOAD = {"seed": 1, "L": (1 << 24) + 37, "betas": (1.0, 1.702, 0.5),
                   "dtypes": ("fp32", "fp16", "bf16")}
+
+
+# The one timed Swish-gradient case on the pages (the Ascend C custom-operator page,
+# performance table): an fp16 activation of shape [32, 64, 56, 56] (6,422,528 elements),
+# plain SiLU backward (beta = 1).  Drawn with the Swish workload's distributions.
+SWISH_CONTEXT = {"seed": 4, "shape": (32, 64, 56, 56), "dtype": "fp16", "beta": 1.0}
 
 
 def _randn(gen: torch.Generator, shape, scale: float) -> torch.Tensor:
