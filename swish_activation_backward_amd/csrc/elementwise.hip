@@ -108,9 +108,10 @@ hipError_t launch_swish_grad(int dtype, const void* grad, const void* x, void* o
 // ------------------------------------------------------------------ b stage
 // Workgroup = 256 lanes laid out as TY rows x TX vector-columns (TX = 2^txlog2).
 // blockIdx.x picks the column strip; blockIdx.y is the walker, which takes the row units
-// blockIdx.y, blockIdx.y + gridDim.y, ... (kBUnitRows rows each).  Inside a unit each
-// lane walks the rows with stride TY; on the vector path it first issues the loads of R
-// rows (3R independent 16-byte loads in flight per lane), then computes and stores them.
+// blockIdx.y, blockIdx.y + gridDim.y, ... (unit_rows rows each, a multiple of R * TY on
+// the vector path).  Inside a unit each lane walks the rows with stride TY; on the vector
+// path it first issues the loads of R rows (3R independent 16-byte loads in flight per
+// lane), then computes and stores them.
 // dg and dfc are written with non-temporal stores: the next stage reads them back from
 // HBM anyway (they are far larger than the caches).  The lane keeps fp32 column sums
 // over all its units; the workgroup reduces them over TY in LDS (fixed order) and writes
@@ -161,7 +162,8 @@ __device__ inline void b_compute(const typename BAccess<T, VECTOR>::Raw& rdy,
 template <typename T, bool VECTOR, int R>
 __global__ __launch_bounds__(256) void b_stage_kernel(const T* dy, const T* g, const T* fc, T* dg,
                                                       T* dfc, float* part, int64_t M, int64_t N,
-                                                      int64_t cv, int64_t nunits, int txlog2) {
+                                                      int64_t cv, int64_t unit_rows,
+                                                      int64_t nunits, int txlog2) {
   using A = BAccess<T, VECTOR>;
   constexpr int V = A::V;
   const int tid = threadIdx.x;
@@ -177,8 +179,8 @@ __global__ __launch_bounds__(256) void b_stage_kernel(const T* dy, const T* g, c
 
   const int64_t col = c * V;
   for (int64_t unit = blockIdx.y; c < cv && unit < nunits; unit += gridDim.y) {
-    const int64_t r0 = unit * kBUnitRows;
-    const int64_t r1 = (r0 + kBUnitRows < M) ? r0 + kBUnitRows : M;
+    const int64_t r0 = unit * unit_rows;
+    const int64_t r1 = (r0 + unit_rows < M) ? r0 + unit_rows : M;
     int64_t r = r0 + ty;
     for (; r + (R - 1) * TY < r1; r += R * TY) {
       typename A::Raw a[R], b[R], d[R];
@@ -270,12 +272,12 @@ static hipError_t b_stage_t(const BPlan& p, const void* dy, const void* g, const
   const T* c = static_cast<const T*>(fc);
   if (p.vec > 1) {
     hipLaunchKernelGGL((b_stage_kernel<T, true, kBRowsInFlight>), grid, dim3(256), 0, stream, a, b, c,
-                       static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.nunits,
-                       txlog2);
+                       static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.unit_rows,
+                       p.nunits, txlog2);
   } else {
     hipLaunchKernelGGL((b_stage_kernel<T, false, 1>), grid, dim3(256), 0, stream, a, b, c,
-                       static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.nunits,
-                       txlog2);
+                       static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.unit_rows,
+                       p.nunits, txlog2);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -14,36 +14,46 @@ inline int vec_of(int dtype) { return 16 / elem_size(dtype); }
 
 // ---------------------------------------------------------------- b stage
 // A workgroup of 256 threads owns a strip of TX vector-columns (TX a power of two
-// <= 64; TY = 256 / TX rows are in flight per step).  The rows are cut into units of
-// kBUnitRows; the workgroups of a strip ("walkers", grid.y of them) take the units
-// round-robin (walker w: units w, w + walkers, ...), a static assignment that keeps the
-// column sums run-to-run deterministic while every walker ends within one unit of the
-// others.  Each walker leaves one fp32 partial row [2N] (dg sums, then dfc sums) in the
-// workspace, which the finalize kernel sums in walker order.
+// <= 32; TY = 256 / TX rows per pass, each lane issuing the loads of kBRowsInFlight rows
+// before it computes them).  The rows are cut into units of unit_rows = max(64,
+// kBRowsInFlight * TY) rows, so a unit is whole passes; the workgroups of a strip
+// ("walkers", grid.y of them) take the units round-robin (walker w: units w, w + walkers,
+// ...), a static assignment that keeps the column sums run-to-run deterministic while
+// every walker ends within one unit of the others.  Each walker leaves one fp32 partial
+// row [2N] (dg sums, then dfc sums) in the workspace, which the finalize kernel sums in
+// walker order.  Measured on MI355X at M = 220000, N = 1024 bf16 (inputs in HBM, finalize
+// included): 32-wide strips, 8 rows in flight and 64-row units with 256 walkers per strip
+// run 384 us; 64-wide strips, 4 rows and 32-row units ran 403-406 us; walker counts that
+// are not a power of two (balanced to whole rounds) ran slower.
 struct BPlan {
   int vec;             // elements per 16-byte access (1 when the scalar path is used)
   int tx, ty;          // thread layout inside the 256-thread workgroup
   int64_t cv;          // vector columns per row = N / vec
   int64_t nstrips;     // ceil(cv / tx)
-  int64_t nunits;      // ceil(M / kBUnitRows)
+  int64_t unit_rows;   // rows per work unit (a multiple of the rows one pass covers)
+  int64_t nunits;      // ceil(M / unit_rows)
   int64_t nwalk;       // walkers per strip (grid.y) = partial rows
   size_t ws_bytes;     // nwalk * 2N * sizeof(float)
 };
 
 constexpr int kBThreads = 256;
-constexpr int64_t kBUnitRows = 32;       // rows per work unit
+constexpr int kBMaxTx = 32;              // widest strip, in 16-byte vector columns
+constexpr int64_t kBMinUnitRows = 64;    // smallest work unit
 constexpr int64_t kBWalkBlocks = 1024;   // resident workgroups to aim for (all strips)
-constexpr int kBRowsInFlight = 4;        // rows whose loads a lane issues before computing
+constexpr int kBRowsInFlight = 8;        // rows whose loads a lane issues before computing
 
 inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
   BPlan p{};
-  // the walker count depends only on (M, N, dtype), never on pointer alignment
+  // the unit size and the walker count depend only on (M, N, dtype), never on pointer
+  // alignment (the workspace query cannot see the pointers)
   const int vref = vec_of(dtype);
   const int64_t cv_ref = (N % vref == 0) ? N / vref : N;
   int tx_ref = 1;
-  while (tx_ref < 64 && tx_ref < cv_ref) tx_ref <<= 1;
+  while (tx_ref < kBMaxTx && tx_ref < cv_ref) tx_ref <<= 1;
   const int64_t strips_ref = ceil_div(cv_ref, tx_ref);
-  p.nunits = M > 0 ? ceil_div(M, kBUnitRows) : 0;
+  const int64_t pass_rows = (int64_t)kBRowsInFlight * (kBThreads / tx_ref);
+  p.unit_rows = pass_rows > kBMinUnitRows ? pass_rows : kBMinUnitRows;
+  p.nunits = M > 0 ? ceil_div(M, p.unit_rows) : 0;
   int64_t nwalk = ceil_div(kBWalkBlocks, strips_ref);
   if (nwalk > p.nunits) nwalk = p.nunits;
   if (nwalk < 1) nwalk = 1;
@@ -53,7 +63,7 @@ inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
   p.vec = (vector_path && N % vref == 0) ? vref : 1;
   p.cv = N / p.vec;
   int tx = 1;
-  while (tx < 64 && tx < p.cv) tx <<= 1;
+  while (tx < kBMaxTx && tx < p.cv) tx <<= 1;
   p.tx = tx;
   p.ty = kBThreads / tx;
   p.nstrips = ceil_div(p.cv, tx);
