@@ -39,7 +39,11 @@ struct BPlan {
 constexpr int kBThreads = 256;
 constexpr int kBMaxTx = 32;              // widest strip, in 16-byte vector columns
 constexpr int64_t kBMinUnitRows = 64;    // smallest work unit
-constexpr int64_t kBWalkBlocks = 1024;   // resident workgroups to aim for (all strips)
+// Workgroups per launch, all strips together, at most: four rounds of one resident
+// workgroup per CU (the vector kernel holds 300 VGPRs).  The walker count per strip is
+// rounded down so that a launch never spills a few workgroups into a fifth round (at
+// N = 14336 bf16, 56 strips x 19 walkers = 1064 workgroups ran 474 us; 56 x 18 fits).
+constexpr int64_t kBWalkBlocks = 1024;
 constexpr int kBRowsInFlight = 8;        // rows whose loads a lane issues before computing
 
 inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
@@ -54,7 +58,7 @@ inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
   const int64_t pass_rows = (int64_t)kBRowsInFlight * (kBThreads / tx_ref);
   p.unit_rows = pass_rows > kBMinUnitRows ? pass_rows : kBMinUnitRows;
   p.nunits = M > 0 ? ceil_div(M, p.unit_rows) : 0;
-  int64_t nwalk = ceil_div(kBWalkBlocks, strips_ref);
+  int64_t nwalk = kBWalkBlocks / strips_ref;
   if (nwalk > p.nunits) nwalk = p.nunits;
   if (nwalk < 1) nwalk = 1;
   p.nwalk = nwalk;

@@ -95,7 +95,8 @@ def test_b_stage_accumulates_into_nonzero_db(dt):
 
 
 @pytest.mark.parametrize("M,N", [(1, 1), (37, 13), (300, 8), (129, 1000), (2, 2056),
-                                 (4097, 24), (5, 4104), (70000, 16)])
+                                 (4097, 24), (5, 4104), (70000, 16), (3001, 200),
+                                 (20000, 120)])
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
 def test_b_stage_odd_shapes(M, N, dt):
     inp = swiglu_inputs(SwiGLUShape("odd", 11, M, 8, N), dtype=dt)
