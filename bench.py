@@ -232,7 +232,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the data-parallel "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the data-parallel "
               "split over M and its all-reduce of db/dw are design notes only); run with "
               "--gpus 1", file=sys.stderr)
         sys.exit(2)
