@@ -154,6 +154,28 @@ def time_swish_context(swg, steps):
                     "cache-evicting write; the pages' times are Ascend 910B, context only"}
 
 
+def measured_copy_rate(reps=10, nbytes=1 << 30):
+    """HBM rate of a plain device-to-device copy (torch copy_, 1 GiB read + 1 GiB written),
+    the practical ceiling the HBM-bound stages are also compared with (context only: the
+    roofline peak stays the 8 TB/s specification)."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return 2.0 * nbytes / t
+
+
 def copy_calibration(nbytes, reps=5):
     """A plain device-to-device copy of `nbytes`, for scaling the HBM byte counters."""
     import torch
@@ -360,6 +382,12 @@ def main():
         "stages": stages,
         "roofline": roof,
     }
+    copy_rate = measured_copy_rate()
+    out["hbm_copy"] = {"GB/s": round(copy_rate / 1e9, 1),
+                       "note": "plain 1 GiB device-to-device copy (torch copy_), read + write bytes"}
+    for n in names:
+        if stages[n]["bound"] == "hbm":
+            stages[n]["frac_of_copy"] = round(work[n]["bytes"] / per_stage[n] / copy_rate, 4)
     out["forward"] = time_forward(swg, d, M, K, N, args.warmup, args.steps)
     out["swish_pages_shape"] = time_swish_context(swg, 20)
     if not args.no_cpu_baseline:
