@@ -103,6 +103,14 @@ __device__ inline SigmoidParts sigmoid_parts(float t) {
   return p;
 }
 
+// sigma(t) alone (the forward's SiLU): 1 / (1 + 2^(-t log2 e)).  Correct for every finite
+// t without the sign split above: for t below about -88 the exponential overflows to
+// +inf and the reciprocal gives 0, the limit of sigma.
+__device__ inline float sigmoid_only(float t) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t * kLog2e));
+}
+
 // s'(t) = sigma(t) (1 + t (1 - sigma(t))) = sigma(t) + t sigma(t)(1 - sigma(t)).
 __device__ inline float swish_factor(float t) {
   const SigmoidParts p = sigmoid_parts(t);

@@ -1195,10 +1195,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                 loff + (uint32_t)(wp * 128 + i * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes;
             const float g0 = acc[i][jj][rr] + bgv, g1 = acc[i][jj][rr + 1] + bgv;
             const float c0 = acc[i][2 + jj][rr] + bfv, c1 = acc[i][2 + jj][rr + 1] + bfv;
-            const SigmoidParts s0 = sigmoid_parts(g0), s1 = sigmoid_parts(g1);
+            const float s0 = sigmoid_only(g0), s1 = sigmoid_only(g1);
             f_store_pair<T>(g0, g1, sel, rgo, voff, okc);
             f_store_pair<T>(c0, c1, sel, rfo, voff, okc);
-            f_store_pair<T>(g0 * s0.s * c0, g1 * s1.s * c1, sel, ryo, voff, okc);
+            f_store_pair<T>(g0 * s0 * c0, g1 * s1 * c1, sel, ryo, voff, okc);
           }
       }
     }
