@@ -154,6 +154,67 @@ def time_swish_context(swg, steps):
                     "cache-evicting write; the pages' times are Ascend 910B, context only"}
 
 
+def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
+    """The b, w and x stages at the other SwiGLU workloads (same seeded recipe), each
+    stage bracketed by its own events, median over `steps` calls.  Reported beside the
+    step (the tiny and ragged shapes are launch- and latency-bound; the LLM-sized FFN is
+    matrix-core bound); not part of `value`."""
+    import torch
+    from workloads.gen import SWIGLU_WORKLOADS, swiglu_inputs
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name in names:
+        shape = SWIGLU_WORKLOADS[name]
+        M, K, N = shape.M, shape.K, shape.N
+        d = {k: v.to(dev) for k, v in swiglu_inputs(shape).items()}
+        dg, dfc = torch.empty_like(d["dy"]), torch.empty_like(d["dy"])
+        db_g = torch.zeros(N, dtype=torch.bfloat16, device=dev)
+        db_fc = torch.zeros_like(db_g)
+        dw_g = torch.zeros(K, N, dtype=torch.bfloat16, device=dev)
+        dw_fc = torch.zeros_like(dw_g)
+        dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+        ws_b = torch.empty(max(1, swg.swiglu_bwd_b_workspace_size(M, N, torch.bfloat16)),
+                           dtype=torch.uint8, device=dev)
+        ws_w = torch.empty(max(1, swg.swiglu_bwd_w_workspace_size(M, K, N, torch.bfloat16)),
+                           dtype=torch.uint8, device=dev)
+        calls = {
+            "b": lambda: swg.swiglu_bwd_b(d["dy"], d["g"], d["fc"], dg, dfc, db_g, db_fc,
+                                          workspace=ws_b),
+            "w": lambda: swg.swiglu_bwd_w(d["x"], dg, dfc, dw_g, dw_fc, workspace=ws_w),
+            "x": lambda: swg.swiglu_bwd_x(dg, dfc, d["w_g"], d["w_fc"], dx),
+        }
+        for _ in range(warmup):
+            for f in calls.values():
+                f()
+        ev = []
+        for _ in range(steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            for i, f in enumerate(calls.values()):
+                f()
+                e[i + 1].record(stream)
+            ev.append(e)
+        torch.cuda.synchronize()
+        work = stage_work(M, K, N, 0)
+        out = {"M": M, "K": K, "N": N}
+        for i, st in enumerate(calls):
+            ts = sorted(e[i].elapsed_time(e[i + 1]) * 1e-3 for e in ev)
+            t = ts[len(ts) // 2]
+            wk = work[st]
+            e = {"median_us": round(t * 1e6, 2), "frac": round(wk["t_roof"] / t, 4),
+                 "bound": wk["bound"]}
+            if wk["flops"]:
+                e["TFLOP/s"] = round(wk["flops"] / t / 1e12, 1)
+            else:
+                e["GB/s"] = round(wk["bytes"] / t / 1e9, 1)
+            out[st] = e
+        res[name] = out
+        del calls, d, dg, dfc, dx, dw_g, dw_fc, ws_b, ws_w
+        torch.cuda.empty_cache()
+    return res
+
+
 def measured_copy_rate(reps=10, nbytes=1 << 30):
     """HBM rate of a plain device-to-device copy (torch copy_, 1 GiB read + 1 GiB written),
     the practical ceiling the HBM-bound stages are also compared with (context only: the
@@ -243,6 +304,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ffn_220k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip timing the b, w and x stages at the other SwiGLU workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration) and exit")
     ap.add_argument("--cpu-rows", type=int, default=1 << 30,
@@ -390,6 +453,8 @@ def main():
             stages[n]["frac_of_copy"] = round(work[n]["bytes"] / per_stage[n] / copy_rate, 4)
     out["forward"] = time_forward(swg, d, M, K, N, args.warmup, args.steps)
     out["swish_pages_shape"] = time_swish_context(swg, 20)
+    if not args.no_per_config:
+        out["per_config"] = time_configs(swg)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, sw_inputs, args.cpu_rows, args.cpu_swish_len)
     print(json.dumps(out), flush=True)
