@@ -39,11 +39,16 @@ struct BPlan {
 constexpr int kBThreads = 256;
 constexpr int kBMaxTx = 32;              // widest strip, in 16-byte vector columns
 constexpr int64_t kBMinUnitRows = 64;    // smallest work unit
-// Workgroups per launch, all strips together, at most: four rounds of one resident
-// workgroup per CU (the vector kernel holds 300 VGPRs).  The walker count per strip is
-// rounded down so that a launch never spills a few workgroups into a fifth round (at
-// N = 14336 bf16, 56 strips x 19 walkers = 1064 workgroups ran 474 us; 56 x 18 fits).
-constexpr int64_t kBWalkBlocks = 1024;
+// Walkers per strip: of the smallest power of two that launches at least kBMinBlocks
+// workgroups in all and the next two (each capped at the number of units), the one that
+// minimises rounds x units per walker, where a round is kBSlots workgroups (one resident
+// per CU of the MI355X: the vector kernel holds 300 VGPRs).  More walkers would also add
+// partial rows for the finalize to read.  Counts that are not a power of two ran
+// slower even when balanced (measured at N = 1024); at N = 14336 bf16 the rule gives 56
+// strips x 32 walkers (seven full rounds of 8 units, 434 us) where 56 x 19 ran 474 us and
+// 56 x 18 441-444 us.
+constexpr int64_t kBSlots = 256;
+constexpr int64_t kBMinBlocks = 1024;
 constexpr int kBRowsInFlight = 8;        // rows whose loads a lane issues before computing
 
 inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
@@ -58,9 +63,21 @@ inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
   const int64_t pass_rows = (int64_t)kBRowsInFlight * (kBThreads / tx_ref);
   p.unit_rows = pass_rows > kBMinUnitRows ? pass_rows : kBMinUnitRows;
   p.nunits = M > 0 ? ceil_div(M, p.unit_rows) : 0;
-  int64_t nwalk = kBWalkBlocks / strips_ref;
-  if (nwalk > p.nunits) nwalk = p.nunits;
-  if (nwalk < 1) nwalk = 1;
+  int64_t nwalk = 1;
+  if (p.nunits > 0) {
+    int64_t w0 = 1;   // smallest power of two reaching kBMinBlocks workgroups
+    while (strips_ref * w0 < kBMinBlocks) w0 *= 2;
+    int64_t best_cost = -1;
+    for (int64_t w = w0; w <= 4 * w0; w *= 2) {
+      const int64_t ww = w < p.nunits ? w : p.nunits;
+      const int64_t cost = ceil_div(strips_ref * ww, kBSlots) * ceil_div(p.nunits, ww);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        nwalk = ww;
+      }
+      if (ww == p.nunits) break;
+    }
+  }
   p.nwalk = nwalk;
   p.ws_bytes = (M > 0 && N > 0) ? (size_t)p.nwalk * (size_t)(2 * N) * sizeof(float) : 0;
 

@@ -208,11 +208,16 @@ def test_workspace_queries():
         nb = b(M, N, torch.bfloat16)
         assert nb % (2 * N * 4) == 0 and 0 < nb // (2 * N * 4) <= max(M, 1)
         assert nb // (2 * N * 4) <= 4096
-    # b plan: strips of at most 32 16-byte vector columns, walkers per strip rounded down
-    # so that strips x walkers <= 1024 (four rounds of one resident workgroup per CU)
-    for (M, N, dt, strips) in ((220000, 1024, torch.bfloat16, 4), (16384, 14336, torch.bfloat16, 56),
-                               (16384, 14336, torch.float32, 112), (8191, 1024, torch.float16, 4),
-                               (4097, 24, torch.bfloat16, 1)):
+    # b plan: strips of at most 32 16-byte vector columns, units of whole 8-row passes, and
+    # a power-of-two walker count per strip (or every unit) chosen for whole rounds of 256
+    # resident workgroups; pinned at the workload shapes
+    for (M, N, dt, strips, walkers) in ((220000, 1024, torch.bfloat16, 4, 256),
+                                        (16384, 14336, torch.bfloat16, 56, 32),
+                                        (16384, 14336, torch.float32, 112, 16),
+                                        (220000, 1024, torch.float32, 8, 128),
+                                        (8191, 1024, torch.float16, 4, 128),
+                                        (256, 128, torch.bfloat16, 1, 2),
+                                        (4097, 24, torch.bfloat16, 1, 9)):
         vec = 4 if dt == torch.float32 else 8
         cv = N // vec if N % vec == 0 else N          # 16-byte vector columns
         tx = 1
@@ -220,9 +225,12 @@ def test_workspace_queries():
             tx *= 2
         assert -(-cv // tx) == strips
         unit = max(64, 8 * (256 // tx))               # rows per unit: whole 8-row passes
-        walkers = b(M, N, dt) // (2 * N * 4)
-        assert walkers == min(1024 // strips, -(-M // unit)), (M, N, dt, walkers)
-        assert walkers * strips <= 1024
+        nunits = -(-M // unit)
+        got = b(M, N, dt) // (2 * N * 4)
+        assert got == walkers, (M, N, dt, got)
+        assert got == nunits or (got & (got - 1)) == 0    # a power of two, or every unit
+        assert strips * got >= 1024 or got == nunits
+        assert strips * got < 8 * max(1024, strips)
     # w: the split-M partials only when the output tile grid is small
     assert w(16384, 4096, 14336, torch.bfloat16) == 0
     s3 = w(220000, 512, 1024, torch.bfloat16)
