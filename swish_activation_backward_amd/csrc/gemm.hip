@@ -968,14 +968,17 @@ __device__ inline void f_read(const uint16_t* slot, int wp, int lane, const int 
 }
 
 // Store one output of the epilogue: values v0 (row R) and v1 (row R + 1) of one column per
-// lane become 32-bit row pairs exactly as in store_tile_rows.
+// lane become 32-bit row pairs exactly as in store_tile_rows.  Non-temporal (cache policy
+// nt): g, fc and y, 1.35 GB at the large-batch shape, are not read again by this kernel,
+// and keeping them out of the caches leaves the x and W panels there (forward 679-683 ->
+// 629-632 us in a same-board comparison; the x stage's dx stores gained nothing from it).
 template <typename T>
 __device__ inline void f_store_pair(float v0, float v1, uint32_t sel, __amdgpu_buffer_rsrc_t r,
                                     uint32_t voff, bool ok) {
   const uint32_t own = pack2<T>(v0, v1);
   const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
   const uint32_t out = __builtin_amdgcn_perm(nb, own, sel);
-  if (ok) __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)voff, 0, 0);
+  if (ok) __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)voff, 0, 2);
 }
 
 // One forward issue: the tile's x window with the stage's first column as soffset, the
