@@ -246,9 +246,11 @@ __global__ __launch_bounds__(NT32) void fwd32_kernel(const float* __restrict__ x
         if (m < M && n < N) {
           const float gv = ag[i][j][r] + bgv, fv = af[i][j][r] + bfv;
           const int64_t o = m * N + n;
-          g[o] = gv;
-          fc[o] = fv;
-          y[o] = gv * sigmoid_parts(gv).s * fv;
+          // written once and not read again here: non-temporal stores keep the x and W
+          // panels in the caches (as in the 16-bit forward)
+          __builtin_nontemporal_store(gv, g + o);
+          __builtin_nontemporal_store(fv, fc + o);
+          __builtin_nontemporal_store(gv * sigmoid_only(gv) * fv, y + o);
         }
       }
     }
