@@ -156,13 +156,16 @@ def time_swish_context(swg, steps):
 
 def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
     """The b, w and x stages at the other SwiGLU workloads (same seeded recipe), each
-    stage bracketed by its own events, median over `steps` calls.  Reported beside the
-    step (the tiny and ragged shapes are launch- and latency-bound; the LLM-sized FFN is
-    matrix-core bound); not part of `value`."""
+    stage call preceded by a 1 GiB write that evicts the 256 MB last-level cache (the
+    tiny and ragged working sets would otherwise stay in it) and bracketed by its own
+    events, median over `steps` calls.  Reported beside the step (the tiny and ragged
+    shapes are launch- and latency-bound; the LLM-sized FFN is matrix-core bound); not
+    part of `value`."""
     import torch
     from workloads.gen import SWIGLU_WORKLOADS, swiglu_inputs
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     res = {}
     for name in names:
         shape = SWIGLU_WORKLOADS[name]
@@ -188,18 +191,19 @@ def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
             for f in calls.values():
                 f()
         ev = []
-        for _ in range(steps):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            e[0].record(stream)
+        for it in range(steps):
+            e = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
             for i, f in enumerate(calls.values()):
+                flush.fill_((it + i) & 0xFF)
+                e[i][0].record(stream)
                 f()
-                e[i + 1].record(stream)
+                e[i][1].record(stream)
             ev.append(e)
         torch.cuda.synchronize()
         work = stage_work(M, K, N, 0)
         out = {"M": M, "K": K, "N": N}
         for i, st in enumerate(calls):
-            ts = sorted(e[i].elapsed_time(e[i + 1]) * 1e-3 for e in ev)
+            ts = sorted(e[i][0].elapsed_time(e[i][1]) * 1e-3 for e in ev)
             t = ts[len(ts) // 2]
             wk = work[st]
             e = {"median_us": round(t * 1e6, 2), "frac": round(wk["t_roof"] / t, 4),
