@@ -68,7 +68,8 @@ typedef enum {
  * current contents and rounded once; the caller zeroes them for a plain gradient.
  * `workspace` must hold swiglu_bwd_b_workspace_size(M, N, dtype) bytes of device memory
  * (fp32 column partials; contents on entry are ignored, contents on return unspecified);
- * it may be NULL when that size is 0.  No aliasing between any two buffers.
+ * it may be NULL when that size is 0.  No output (dg, dfc, db_g, db_fc, workspace) may
+ * overlap another buffer (SWG_ERR_INVALID); the inputs are only read and may share memory.
  */
 swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc,
                         void* dg, void* dfc, void* db_g, void* db_fc,
@@ -88,7 +89,8 @@ size_t swiglu_bwd_b_workspace_size(int64_t M, int64_t N, swg_dtype dtype);
  * cores, accumulated in fp32 (split over M in fixed-order fp32 partials when the output is
  * small), added to the current dw and rounded once (fp32: not rounded): dw is ACCUMULATED
  * like db.  `workspace` holds swiglu_bwd_w_workspace_size(M, K, N, dtype) bytes (0 when
- * no split is needed; the same for every dtype).
+ * no split is needed; the same for every dtype).  dw_g, dw_fc and the workspace may not
+ * overlap each other or an input (SWG_ERR_INVALID).
  */
 swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc,
                         void* dw_g, void* dw_fc,
@@ -102,7 +104,8 @@ size_t swiglu_bwd_w_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dt
  * dg, dfc: [M, N]; w_g, w_fc: [K, N] (row-major, as on the page); dx: [M, K], OVERWRITTEN.
  * dtype: bf16, fp16 or fp32; K and N multiples of 8 (bf16 / fp16) or of 4 (fp32) and
  * below 2^22, M below 2^31, every pointer 16-byte aligned (else SWG_ERR_UNSUPPORTED).  fp32 accumulation, one rounding
- * (none for fp32).  N = 0 with M*K > 0 writes dx = 0 (the empty sum).
+ * (none for fp32).  N = 0 with M*K > 0 writes dx = 0 (the empty sum).  dx may not overlap
+ * an input (SWG_ERR_INVALID).
  */
 swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
                         void* dx, int64_t M, int64_t K, int64_t N, swg_dtype dtype,
@@ -121,7 +124,8 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
  * its element size: SWG_ERR_INVALID).  Products on the matrix cores with fp32 accumulation; the bias is
  * added in fp32; y is formed from the fp32 values of g and fc (before their rounding); each
  * output is rounded once (fp32: not rounded).  K = 0 gives g = b_g, fc = b_fc (the empty sums); x, w_g and
- * w_fc may then be NULL.  No aliasing between any two buffers.
+ * w_fc may then be NULL.  g, fc and y may not overlap each other or an input
+ * (SWG_ERR_INVALID).
  */
 swg_status swiglu_fwd(const void* x, const void* w_g, const void* w_fc,
                       const void* b_g, const void* b_fc, void* g, void* fc, void* y,

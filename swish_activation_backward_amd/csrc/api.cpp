@@ -31,6 +31,43 @@ swg_status hip_status(hipError_t e) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// A buffer as a byte range [p, p + bytes); bytes = 0 marks an absent buffer.
+struct Span {
+  const void* p;
+  int64_t bytes;
+};
+
+// rows x cols elements of es bytes; -1 when the byte count overflows int64
+int64_t span_bytes(int64_t rows, int64_t cols, int64_t es) {
+  int64_t n;
+  if (__builtin_mul_overflow(rows, cols, &n) || __builtin_mul_overflow(n, es, &n)) return -1;
+  return n;
+}
+
+bool spans_meet(const Span& a, const Span& b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes <= 0 || b.bytes <= 0) return false;
+  const __int128 a0 = (__int128)reinterpret_cast<uintptr_t>(a.p), b0 =
+      (__int128)reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Every output span must be disjoint from every other span (inputs may share memory with
+// each other: they are only read).  False also when a byte count overflowed.
+template <size_t NO, size_t NI>
+bool outputs_disjoint(const Span (&outs)[NO], const Span (&ins)[NI]) {
+  for (const Span& o : outs)
+    if (o.bytes < 0) return false;
+  for (const Span& i : ins)
+    if (i.bytes < 0) return false;
+  for (size_t a = 0; a < NO; ++a) {
+    for (size_t b = a + 1; b < NO; ++b)
+      if (spans_meet(outs[a], outs[b])) return false;
+    for (size_t b = 0; b < NI; ++b)
+      if (spans_meet(outs[a], ins[b])) return false;
+  }
+  return true;
+}
+
 // Compute units of the current device (cached per device; 0 if the query fails, in
 // which case the launch uses one workgroup per tile).
 constexpr int kMaxDevices = 64;
@@ -236,6 +273,13 @@ swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc, void* dg,
   if (workspace_bytes < p.ws_bytes) return SWG_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
   if (!aligned(workspace, 16)) return SWG_ERR_INVALID;
+  {
+    const int64_t t = span_bytes(M, N, (int64_t)es), v = span_bytes(1, N, (int64_t)es);
+    const Span outs[] = {{dg, t}, {dfc, t}, {db_g, v}, {db_fc, v},
+                         {workspace, (int64_t)p.ws_bytes}};
+    const Span ins[] = {{dy, t}, {g, t}, {fc, t}};
+    if (!outputs_disjoint(outs, ins)) return SWG_ERR_INVALID;
+  }
   return hip_status(launch_b_stage(dtype, p, dy, g, fc, dg, dfc, db_g, db_fc, M, N,
                                    static_cast<float*>(workspace), as_stream(stream)));
 }
@@ -273,6 +317,13 @@ swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc, void* dw
   if (workspace_bytes < p.ws_bytes) return SWG_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
   if (!aligned(workspace, 16)) return SWG_ERR_INVALID;
+  {
+    const int64_t es = elem_size(dtype);
+    const int64_t w = span_bytes(K, N, es), d = span_bytes(M, N, es);
+    const Span outs[] = {{dw_g, w}, {dw_fc, w}, {workspace, (int64_t)p.ws_bytes}};
+    const Span ins[] = {{x, span_bytes(M, K, es)}, {dg, d}, {dfc, d}};
+    if (!outputs_disjoint(outs, ins)) return SWG_ERR_INVALID;
+  }
   return hip_status(launch_w_stage(dtype, p, x, dg, dfc, dw_g, dw_fc, M, K, N,
                                    static_cast<float*>(workspace), gemm_grid_cap(),
                                    as_stream(stream)));
@@ -290,6 +341,13 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
                                   as_stream(stream)));
   if (!dg || !dfc || !w_g || !w_fc) return SWG_ERR_NULLPTR;
   for (const void* p : {dg, dfc, w_g, w_fc}) if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
+  {
+    const int64_t es = elem_size(dtype);
+    const int64_t d = span_bytes(M, N, es), w = span_bytes(K, N, es);
+    const Span outs[] = {{dx, span_bytes(M, K, es)}};
+    const Span ins[] = {{dg, d}, {dfc, d}, {w_g, w}, {w_fc, w}};
+    if (!outputs_disjoint(outs, ins)) return SWG_ERR_INVALID;
+  }
   return hip_status(launch_x_stage(dtype, dg, dfc, w_g, w_fc, dx, M, K, N, gemm_grid_cap(),
                                    as_stream(stream)));
 }
@@ -307,6 +365,13 @@ swg_status swiglu_fwd(const void* x, const void* w_g, const void* w_fc, const vo
     if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
   for (const void* p : {b_g, b_fc})
     if (!aligned(p, (size_t)elem_size(dtype))) return SWG_ERR_INVALID;
+  {
+    const int64_t es = elem_size(dtype);
+    const int64_t o = span_bytes(M, N, es), w = span_bytes(K, N, es), v = span_bytes(1, N, es);
+    const Span outs[] = {{g, o}, {fc, o}, {y, o}};
+    const Span ins[] = {{x, span_bytes(M, K, es)}, {w_g, w}, {w_fc, w}, {b_g, v}, {b_fc, v}};
+    if (!outputs_disjoint(outs, ins)) return SWG_ERR_INVALID;
+  }
   return hip_status(launch_fwd(dtype, x, w_g, w_fc, b_g, b_fc, g, fc, y, M, K, N,
                                gemm_grid_cap(), as_stream(stream)));
 }

@@ -11,7 +11,8 @@ Three checks are applied to every output tensor:
 2. a per-element mixed bound |gpu - ref| <= rtol * |ref| + E, where E is the
    rounding model of the arithmetic that produced the value (fp32 math + one final
    rounding).  This binds where atol = 1e-4 exceeds the outputs themselves;
-3. a normwise bound ||gpu - ref||_2 <= nw * ||ref||_2.
+3. a normwise bound ||gpu - ref||_2 <= nw * ||ref||_2 (bf16: 2^-8, the unit roundoff of
+   an 8-bit significand; a correctly rounded bf16 tensor sits near 0.4 * 2^-8).
 
 ``Checker`` accumulates the three over chunks so that large tensors can be compared
 piecewise; ``compare`` is the one-shot form.
@@ -29,7 +30,9 @@ FP32_RTOL = 1e-5
 FP16_SUBNORMAL_HALF = 2.0 ** -25
 
 RTOL = {"bf16": BF16_RTOL, "fp16": FP16_RTOL, "fp32": FP32_RTOL}
-NORMWISE = {"bf16": 2.0 ** -7, "fp16": 2.0 ** -10, "fp32": 2.0 ** -20}
+NORMWISE = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -10, "fp32": 2.0 ** -20}
+# unit roundoff of each storage type (RNE): the relative error of one rounding
+STORAGE_UNIT = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11, "fp32": 2.0 ** -24}
 TORCH_NAME = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}
 
 
@@ -73,6 +76,14 @@ def dfc_abs_model(dy, g):
 def sum_abs_model(abs_sum):
     """fp32 accumulation of a sum whose magnitude sum is ``abs_sum``."""
     return 2.0 ** -16 * np.asarray(abs_sum, dtype=np.float64)
+
+
+def chained_abs_model(abs_sum, dtype):
+    """A sum of products whose operand was itself a rounded output of an earlier stage
+    (the w and x stages fed by the b stage's dg and dfc, stored in ``dtype``): each operand
+    element carries a relative error of at most the storage unit roundoff u, so the
+    result moves by at most u * A on top of the fp32 accumulation, A the magnitude sum."""
+    return (STORAGE_UNIT[dtype] + 2.0 ** -16) * np.asarray(abs_sum, dtype=np.float64)
 
 
 class ParityError(AssertionError):

@@ -196,6 +196,43 @@ def test_forward_argument_errors(lib):
     assert lib.swiglu_fwd(*fa(bg=ctypes.c_void_p(0x40001))) == INVALID
 
 
+def test_overlapping_outputs_are_rejected(lib):
+    """An output that overlaps another buffer is refused on the host (each call below is
+    otherwise valid, so only the overlap rule can reject it: none reaches a launch)."""
+    M, K, N = 4, 8, 8                      # 64-byte [M, N] tensors, fake buffers 64 KiB apart
+    ba = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                       (("dy", P), ("g", Q), ("fc", R), ("dg", S), ("dfc", T), ("dbg", U),
+                        ("dbfc", V), ("M", M), ("N", N), ("dt", BF16),
+                        ("w", ctypes.c_void_p(0x90000)), ("wb", 1 << 20), ("s", NULL))]
+    for k, alias in (("dg", P), ("dfc", Q), ("dg", ctypes.c_void_p(0x10010)), ("dbg", S),
+                     ("dbfc", ctypes.c_void_p(0x50008)), ("dfc", S), ("w", T), ("w", P)):
+        assert lib.swiglu_bwd_b(*ba(**{k: alias})) == INVALID, (k, alias)
+    wa = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                       (("x", P), ("dg", Q), ("dfc", R), ("dwg", S), ("dwfc", T), ("M", M),
+                        ("K", K), ("N", N), ("dt", BF16), ("w", U), ("wb", 1 << 20),
+                        ("s", NULL))]
+    for k, alias in (("dwg", P), ("dwfc", R), ("dwfc", S), ("dwg", ctypes.c_void_p(0x20010))):
+        assert lib.swiglu_bwd_w(*wa(**{k: alias})) == INVALID, (k, alias)
+    # a split over M (4096 rows, 2 x 1 tiles): the workspace is used and may not overlap dw
+    import torch
+    need = swg.swiglu_bwd_w_workspace_size(4096, K, N, torch.bfloat16)
+    assert need > 0
+    assert lib.swiglu_bwd_w(*wa(M=4096, w=S, wb=need)) == INVALID
+    xa = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                       (("dg", P), ("dfc", Q), ("wg", R), ("wfc", S), ("dx", T), ("M", M),
+                        ("K", K), ("N", N), ("dt", BF16), ("s", NULL))]
+    for alias in (P, Q, R, S, ctypes.c_void_p(0x40030)):
+        assert lib.swiglu_bwd_x(*xa(dx=alias)) == INVALID, alias
+    W_ = ctypes.c_void_p(0x80000)
+    fa = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                       (("x", P), ("wg", Q), ("wfc", R), ("bg", S), ("bfc", T), ("g", U),
+                        ("fc", V), ("y", W_), ("M", M), ("K", K), ("N", N), ("dt", BF16),
+                        ("s", NULL))]
+    for k, alias in (("g", P), ("fc", U), ("y", V), ("y", S), ("g", ctypes.c_void_p(0x50000)),
+                     ("fc", ctypes.c_void_p(0x20020))):
+        assert lib.swiglu_fwd(*fa(**{k: alias})) == INVALID, (k, alias)
+
+
 def test_workspace_queries():
     import torch
     b = swg.swiglu_bwd_b_workspace_size

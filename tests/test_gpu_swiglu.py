@@ -10,7 +10,8 @@ import torch
 import oracle.ref as R
 import swish_activation_backward_amd as swg
 from gpu_util import Guarded, device, note, oracle_b_chunked, oracle_w_chunked, oracle_x_rows, rne
-from parity import Checker, compare, sum_abs_model, to64
+from parity import (Checker, chained_abs_model, compare, dfc_abs_model, dg_abs_model,
+                    sum_abs_model, to64)
 from workloads.gen import DTYPES, SwiGLUShape, swiglu_inputs
 
 pytestmark = pytest.mark.gpu
@@ -225,12 +226,22 @@ def test_chained_b_w_x_on_ragged_batch():
     swg.swiglu_bwd_w(d["x"], dg, dfc, dw_g, dw_fc)
     swg.swiglu_bwd_x(dg, dfc, d["w_g"], d["w_fc"], dx)
     torch.cuda.synchronize()
-    ref = R.swiglu_bwd_ref(to64(inp["dy"]), to64(inp["x"]), to64(inp["w_g"]), to64(inp["w_fc"]),
-                           to64(inp["g"]), to64(inp["fc"]))
+    dy64, g64, fc64, x64 = (to64(inp[k]) for k in ("dy", "g", "fc", "x"))
+    wg64, wf64 = to64(inp["w_g"]), to64(inp["w_fc"])
+    ref = R.swiglu_bwd_ref(dy64, x64, wg64, wf64, g64, fc64)
+    # rounding models: dg, dfc element-wise; db from the fp32 values of dg / dfc; dw and dx
+    # from the bf16 dg / dfc the b stage stored (one storage rounding per operand element)
+    adg, adfc = np.abs(ref["dg"]), np.abs(ref["dfc"])
+    ax = np.abs(x64)
+    models = {"dg": dg_abs_model(dy64, g64, fc64), "dfc": dfc_abs_model(dy64, g64),
+              "db_g": sum_abs_model(adg.sum(0)), "db_fc": sum_abs_model(adfc.sum(0)),
+              "dw_g": chained_abs_model(ax.T @ adg, "bf16"),
+              "dw_fc": chained_abs_model(ax.T @ adfc, "bf16"),
+              "dx": chained_abs_model(adg @ np.abs(wg64).T + adfc @ np.abs(wf64).T, "bf16")}
     got = {"dg": dg, "dfc": dfc, "db_g": db_g, "db_fc": db_fc, "dw_g": dw_g, "dw_fc": dw_fc,
            "dx": dx}
     for k, v in got.items():
-        compare(f"chained {k}", v.cpu(), ref[k], "bf16")
+        compare(f"chained {k}", v.cpu(), ref[k], "bf16", model_abs=models[k])
 
 
 def test_bitwise_deterministic_reruns():

@@ -153,6 +153,29 @@ def pin_swiglu_autograd(b_ref, w_ref, x_ref):
             np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-13)
 
 
+def pin_swiglu_chain(swiglu_bwd_ref):
+    """The chained backward (b, then w and x on the dg and dfc that b produced) against
+    torch.autograd in float64 of y = SiLU(xW_g+b_g)*(xW_fc+b_fc): all seven gradients,
+    each under its own name, at three shapes (non-square, N != K, M > K)."""
+    for (M, K, N, seed) in ((5, 3, 4, 0), (37, 19, 23, 1), (64, 8, 16, 2)):
+        c = _swiglu_case(M, K, N, seed)
+        leaves = {k: c[k].clone().requires_grad_(True) for k in ("x", "w_g", "w_fc", "b_g", "b_fc")}
+        g = leaves["x"] @ leaves["w_g"] + leaves["b_g"]
+        fc = leaves["x"] @ leaves["w_fc"] + leaves["b_fc"]
+        g.retain_grad()
+        fc.retain_grad()
+        y = torch.nn.functional.silu(g) * fc
+        (y * c["dy"]).sum().backward()
+        out = swiglu_bwd_ref(c["dy"].numpy(), c["x"].numpy(), c["w_g"].numpy(),
+                             c["w_fc"].numpy(), g.detach().numpy(), fc.detach().numpy())
+        want = {"dg": g.grad, "dfc": fc.grad, "db_g": leaves["b_g"].grad,
+                "db_fc": leaves["b_fc"].grad, "dw_g": leaves["w_g"].grad,
+                "dw_fc": leaves["w_fc"].grad, "dx": leaves["x"].grad}
+        assert set(out) == set(want)
+        for k, v in want.items():
+            np.testing.assert_allclose(out[k], v.numpy(), rtol=1e-11, atol=1e-13, err_msg=k)
+
+
 def pin_swiglu_fd(b_ref, w_ref, x_ref):
     """Central differences of L = sum(dy * SiLU(xW_g+b_g) * (xW_fc+b_fc)) in mpmath."""
     M, K, N = 4, 3, 5
@@ -268,6 +291,10 @@ def test_swiglu_pins(pin):
     pin(R.b_ref, R.w_ref, R.x_ref)
 
 
+def test_swiglu_chain_pin():
+    pin_swiglu_chain(R.swiglu_bwd_ref)
+
+
 def test_forward_ref_matches_definition():
     rng = np.random.default_rng(2)
     x, w_g, w_fc = rng.normal(size=(4, 3)), rng.normal(size=(3, 5)), rng.normal(size=(3, 5))
@@ -282,8 +309,6 @@ def test_forward_ref_matches_definition():
             sf = b_fc[n] + sum(x[m, k] * w_fc[k, n] for k in range(3))
             assert abs(g[m, n] - sg) <= 1e-12 * (1 + abs(sg))
             assert abs(fc[m, n] - sf) <= 1e-12 * (1 + abs(sf))
-    out = R.swiglu_bwd_ref(rng.normal(size=(4, 5)), x, w_g, w_fc, g, fc)
-    assert set(out) == {"dg", "dfc", "db_g", "db_fc", "dw_g", "dw_fc", "dx"}
 
 
 # ----------------------------------------------------------------------------------
@@ -400,3 +425,35 @@ def test_planted_swiglu_mistake_is_caught(stage, kind):
                                             "x": _x_variant}[stage](kind)
     # the FD pin is slow; the others suffice to catch every planted mistake
     assert _fails_some([p for p in SWIGLU_PINS if p is not pin_swiglu_fd], *fns)
+
+
+def _chain_variant(kind):
+    """The chained backward with one plausible mistake in how the stages are wired."""
+    def f(dy, x, w_g, w_fc, g, fc):
+        if kind == "swap_g_fc":             # b stage given fc as the gate
+            dg, dfc, db_g, db_fc = R.b_ref(dy, fc, g)
+        else:
+            dg, dfc, db_g, db_fc = R.b_ref(dy, g, fc)
+        if kind == "swap_dg_dfc_into_w":
+            dw_g, dw_fc = R.w_ref(x, dfc, dg)
+        else:
+            dw_g, dw_fc = R.w_ref(x, dg, dfc)
+        if kind == "swap_weights_in_x":
+            dx = R.x_ref(dg, dfc, w_fc, w_g)
+        elif kind == "x_from_dg_only":
+            dx = R.x_ref(dg, 0 * dfc, w_g, w_fc)
+        else:
+            dx = R.x_ref(dg, dfc, w_g, w_fc)
+        out = {"dg": dg, "dfc": dfc, "db_g": db_g, "db_fc": db_fc,
+               "dw_g": dw_g, "dw_fc": dw_fc, "dx": dx}
+        if kind == "swap_db":
+            out["db_g"], out["db_fc"] = db_fc, db_g
+        return out
+    return f
+
+
+@pytest.mark.parametrize("kind", ["swap_g_fc", "swap_dg_dfc_into_w", "swap_weights_in_x",
+                                  "x_from_dg_only", "swap_db"])
+def test_planted_chain_mistake_is_caught(kind):
+    with pytest.raises(AssertionError):
+        pin_swiglu_chain(_chain_variant(kind))
