@@ -78,6 +78,26 @@ swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc,
 size_t swiglu_bwd_b_workspace_size(int64_t M, int64_t N, swg_dtype dtype);
 
 /*
+ * The b stage for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation,
+ * kernels and results as swiglu_bwd_b, bit for bit, with the fp32 column partials kept
+ * in a static device array of SWG_B_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends, instead of a caller workspace.  The call itself
+ * allocates nothing (no hipMalloc, no allocating library routine).  Its first call on a
+ * device resolves that device's array address once.  Shapes whose partials exceed the
+ * array (swiglu_bwd_b_workspace_size(M, N, dtype) > SWG_B_SCRATCH_BYTES, i.e. N above 2^21)
+ * return SWG_ERR_WORKSPACE; the other errors are those of swiglu_bwd_b.
+ * Every call on one GPU uses that GPU's one array: two calls that run at the same time on
+ * one GPU (on different streams, or from different threads) race on it and give wrong
+ * db; serialise them on one stream.  The array is fully rewritten by each call (nothing
+ * in it has to start at zero).
+ */
+#define SWG_B_SCRATCH_BYTES (16u << 20)
+swg_status swiglu_bwd_b_noalloc(const void* dy, const void* g, const void* fc,
+                                void* dg, void* dfc, void* db_g, void* db_fc,
+                                int64_t M, int64_t N, swg_dtype dtype, void* stream);
+
+/*
  * w stage [SwiGLU page, formula 3; kernel 2]:  [dw_g | dw_fc] += x^T [dg | dfc]
  * one GEMM [K, M] x [M, 2N] whose right operand is the column concatenation of dg and dfc.
  *   dw_g[k,n]  = RNE(dw_g[k,n]  + sum_m x[m,k] * dg[m,n])

@@ -14,7 +14,7 @@ import threading
 import torch
 
 __all__ = ["SwgError", "load_library", "library_path", "swish_grad", "swish_grad_strided",
-           "swiglu_bwd_b", "swiglu_bwd_w", "swiglu_bwd_x", "swiglu_fwd",
+           "swiglu_bwd_b", "swiglu_bwd_b_noalloc", "swiglu_bwd_w", "swiglu_bwd_x", "swiglu_fwd",
            "swiglu_bwd_b_workspace_size", "swiglu_bwd_w_workspace_size", "swg_version",
            "DTYPE_CODE", "STATUS"]
 
@@ -63,6 +63,8 @@ def load_library():
         lib.swish_grad_strided.restype = i32
         lib.swiglu_bwd_b.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp]
         lib.swiglu_bwd_b.restype = i32
+        lib.swiglu_bwd_b_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp]
+        lib.swiglu_bwd_b_noalloc.restype = i32
         lib.swiglu_bwd_b_workspace_size.argtypes = [i64, i64, i32]
         lib.swiglu_bwd_b_workspace_size.restype = sz
         lib.swiglu_bwd_w.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
@@ -236,6 +238,27 @@ def swiglu_bwd_b(dy, g, fc, dg, dfc, db_g, db_fc, workspace=None, stream=None):
                               _ptr(db_fc), M, N, code, _ptr(ws), 0 if ws is None else
                               ws.numel() * ws.element_size(), _stream(stream, dev))
     _check("swiglu_bwd_b", st, lib)
+
+
+def swiglu_bwd_b_noalloc(dy, g, fc, dg, dfc, db_g, db_fc, stream=None):
+    """b stage with the column partials in the library's static device array (no
+    workspace, no allocation); same results as ``swiglu_bwd_b``."""
+    lib = load_library()
+    if dy.dim() != 2:
+        raise ValueError("dy must be [M, N]")
+    M, N = dy.shape
+    dt, dev = dy.dtype, dy.device
+    for name, t in (("dy", dy), ("g", g), ("fc", fc), ("dg", dg), ("dfc", dfc)):
+        _dense(name, t, dt, (M, N), dev)
+    for name, t in (("db_g", db_g), ("db_fc", db_fc)):
+        if t.numel() != N:
+            raise ValueError(f"{name} must hold N = {N} elements")
+        _dense(name, t, dt, t.shape, dev)
+    with _on_device(dev):
+        st = lib.swiglu_bwd_b_noalloc(_ptr(dy), _ptr(g), _ptr(fc), _ptr(dg), _ptr(dfc),
+                                      _ptr(db_g), _ptr(db_fc), M, N, _dtype_code(dy),
+                                      _stream(stream, dev))
+    _check("swiglu_bwd_b_noalloc", st, lib)
 
 
 def swiglu_bwd_w(x, dg, dfc, dw_g, dw_fc, workspace=None, stream=None):

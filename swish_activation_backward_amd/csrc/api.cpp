@@ -257,9 +257,12 @@ size_t swiglu_bwd_b_workspace_size(int64_t M, int64_t N, swg_dtype dtype) {
   return plan_b(M, N, dtype, true).ws_bytes;
 }
 
-swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc, void* dg, void* dfc,
-                        void* db_g, void* db_fc, int64_t M, int64_t N, swg_dtype dtype,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+// Argument checks shared by swiglu_bwd_b and swiglu_bwd_b_noalloc (workspace: the
+// caller's, or NULL with ws_bytes 0 for the static scratch); fills the plan.
+static swg_status b_checks(const void* dy, const void* g, const void* fc, void* dg, void* dfc,
+                           void* db_g, void* db_fc, int64_t M, int64_t N, int dtype,
+                           const void* workspace, size_t workspace_bytes, bool own_ws,
+                           BPlan* plan) {
   if (!dtype_ok(dtype) || M < 0 || N < 0) return SWG_ERR_INVALID;
   if (M == 0 || N == 0) return SWG_OK;  // dg/dfc empty; db += empty sum
   if (!dy || !g || !fc || !dg || !dfc || !db_g || !db_fc) return SWG_ERR_NULLPTR;
@@ -269,19 +272,46 @@ swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc, void* dg,
     if (!aligned(p, es)) return SWG_ERR_INVALID;
   const bool vec = aligned(dy, 16) && aligned(g, 16) && aligned(fc, 16) && aligned(dg, 16) &&
                    aligned(dfc, 16);
-  const BPlan p = plan_b(M, N, dtype, vec);
-  if (workspace_bytes < p.ws_bytes) return SWG_ERR_WORKSPACE;
-  if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
-  if (!aligned(workspace, 16)) return SWG_ERR_INVALID;
-  {
-    const int64_t t = span_bytes(M, N, (int64_t)es), v = span_bytes(1, N, (int64_t)es);
-    const Span outs[] = {{dg, t}, {dfc, t}, {db_g, v}, {db_fc, v},
-                         {workspace, (int64_t)p.ws_bytes}};
-    const Span ins[] = {{dy, t}, {g, t}, {fc, t}};
-    if (!outputs_disjoint(outs, ins)) return SWG_ERR_INVALID;
+  *plan = plan_b(M, N, dtype, vec);
+  if (own_ws) {
+    if (workspace_bytes < plan->ws_bytes) return SWG_ERR_WORKSPACE;
+    if (plan->ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
+    if (!aligned(workspace, 16)) return SWG_ERR_INVALID;
+  } else if (plan->ws_bytes > kBScratchBytes) {
+    return SWG_ERR_WORKSPACE;   // the partials would not fit the static scratch
   }
+  const int64_t t = span_bytes(M, N, (int64_t)es), v = span_bytes(1, N, (int64_t)es);
+  const Span outs[] = {{dg, t}, {dfc, t}, {db_g, v}, {db_fc, v},
+                       {own_ws ? workspace : nullptr, (int64_t)plan->ws_bytes}};
+  const Span ins[] = {{dy, t}, {g, t}, {fc, t}};
+  if (!outputs_disjoint(outs, ins)) return SWG_ERR_INVALID;
+  return SWG_OK;
+}
+
+swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc, void* dg, void* dfc,
+                        void* db_g, void* db_fc, int64_t M, int64_t N, swg_dtype dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  BPlan p{};
+  const swg_status st = b_checks(dy, g, fc, dg, dfc, db_g, db_fc, M, N, dtype, workspace,
+                                 workspace_bytes, true, &p);
+  if (st != SWG_OK || M == 0 || N == 0) return st;
   return hip_status(launch_b_stage(dtype, p, dy, g, fc, dg, dfc, db_g, db_fc, M, N,
                                    static_cast<float*>(workspace), as_stream(stream)));
+}
+
+swg_status swiglu_bwd_b_noalloc(const void* dy, const void* g, const void* fc, void* dg,
+                                void* dfc, void* db_g, void* db_fc, int64_t M, int64_t N,
+                                swg_dtype dtype, void* stream) {
+  BPlan p{};
+  const swg_status st = b_checks(dy, g, fc, dg, dfc, db_g, db_fc, M, N, dtype, nullptr, 0,
+                                 false, &p);
+  if (st != SWG_OK || M == 0 || N == 0) return st;
+  // every walker writes its whole partial row, so the scratch needs no clearing
+  float* part = nullptr;
+  const hipError_t e = b_scratch(&part);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_b_stage(dtype, p, dy, g, fc, dg, dfc, db_g, db_fc, M, N, part,
+                                   as_stream(stream)));
 }
 
 // ------------------------------------------------------------------- GEMM stages

@@ -10,12 +10,44 @@
 // Both streaming kernels read each input once with 16-byte non-temporal loads
 // (8 bf16/fp16 or 4 fp32 per lane, so one wave instruction moves 1 KiB), keep several
 // independent loads in flight per lane, and write each output once.
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace swg {
+
+// ------------------------------------------------------------------ b-stage scratch
+// Column partials of the b stage for callers that cannot allocate (swiglu_bwd_b_noalloc):
+// a file-scope device array, one copy per GPU, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address hipGetSymbolAddress returns, resolved once per
+// device with that device current.
+static __device__ __align__(256) float scratch[kBScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+hipError_t b_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------ swish_grad
 // grid-stride over 16-byte vectors; U vectors per lane per step, coalesced so that a

@@ -27,6 +27,10 @@ hipError_t launch_swish_grad_strided(int dtype, const void* grad, const void* x,
                                      const StridedView& v, int64_t n, float beta,
                                      hipStream_t stream);
 
+// The device address of the b stage's static scratch array on the current device
+// (kBScratchBytes; resolved on the first call per device, no allocation).
+hipError_t b_scratch(float** out);
+
 hipError_t launch_b_stage(int dtype, const BPlan& p, const void* dy, const void* g,
                           const void* fc, void* dg, void* dfc, void* db_g, void* db_fc,
                           int64_t M, int64_t N, float* part, hipStream_t stream);

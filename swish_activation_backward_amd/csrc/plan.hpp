@@ -48,6 +48,9 @@ constexpr int64_t kBMinUnitRows = 64;    // smallest work unit
 // strips x 32 walkers (seven full rounds of 8 units, 434 us) where 56 x 19 ran 474 us and
 // 56 x 18 441-444 us.
 constexpr int64_t kBSlots = 256;
+// Size of the static partial-row array used by swiglu_bwd_b_noalloc (16 MiB: every shape
+// up to N = 2^21 columns fits; at N = 1024 the plan needs 2 MiB, at N = 14336 3.5 MiB).
+constexpr size_t kBScratchBytes = size_t(16) << 20;
 constexpr int64_t kBMinBlocks = 1024;
 constexpr int kBRowsInFlight = 8;        // rows whose loads a lane issues before computing
 

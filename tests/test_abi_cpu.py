@@ -34,6 +34,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)   # preprocessor lines
     return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)))
 
 
@@ -194,6 +195,32 @@ def test_forward_argument_errors(lib):
         assert lib.swiglu_fwd(*fa(**{k: NULL})) == NULLPTR, k
     assert lib.swiglu_fwd(*fa(x=ctypes.c_void_p(0x10008))) == UNSUPPORTED
     assert lib.swiglu_fwd(*fa(bg=ctypes.c_void_p(0x40001))) == INVALID
+
+
+def test_noalloc_b_stage_argument_errors(lib):
+    """The static-scratch b stage validates like swiglu_bwd_b, and refuses shapes whose
+    partials exceed its array (before any launch)."""
+    import torch
+    M, N = 1000, 64
+    args = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                         (("dy", P), ("g", Q), ("fc", R), ("dg", S), ("dfc", T), ("dbg", U),
+                          ("dbfc", V), ("M", M), ("N", N), ("dt", BF16), ("s", NULL))]
+    f = lib.swiglu_bwd_b_noalloc
+    assert f(*args(M=0)) == OK
+    assert f(*args(N=0, dy=NULL)) == OK
+    assert f(*args(M=-1)) == INVALID
+    assert f(*args(dt=3)) == INVALID
+    for k in ("dy", "g", "fc", "dg", "dfc", "dbg", "dbfc"):
+        assert f(*args(**{k: NULL})) == NULLPTR, k
+    assert f(*args(dbg=ctypes.c_void_p(0x60001))) == INVALID
+    assert f(*args(M=4, N=8, dg=P)) == INVALID                         # output overlaps dy
+    # partials beyond the 16 MiB array: N = 2^22 bf16 columns need one walker's 2N floats
+    big_n = 1 << 22
+    assert swg.swiglu_bwd_b_workspace_size(8192, 1 << 21, torch.bfloat16) <= 16 << 20
+    assert swg.swiglu_bwd_b_workspace_size(8192, big_n, torch.bfloat16) > 16 << 20
+    assert f(*args(M=8192, N=big_n)) == WORKSPACE
+    assert swg.swiglu_bwd_b_workspace_size(220000, 1024, torch.bfloat16) <= 16 << 20
+    assert swg.swiglu_bwd_b_workspace_size(16384, 14336, torch.bfloat16) <= 16 << 20
 
 
 def test_overlapping_outputs_are_rejected(lib):
