@@ -15,7 +15,13 @@ Each stage's absolute GB/s or TFLOP/s is listed too.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 Defaults: 5 warm-up steps, 50 timed steps; per stage the mean (us), median, min and max
-of the per-step event times are reported.
+of the per-step kernel spans are reported.
+
+Stage times are kernel spans: each library call is timed with swg_time_next_call, whose
+HIP events are attached to the call's first and last kernel dispatch on the stream it
+launches on (start of the first kernel to end of the last), the in-process equivalent of
+a kernel trace.  Events recorded around each call are kept as `event_us` (they add the
+dispatch gap, a few microseconds per call).
 """
 from __future__ import annotations
 
@@ -93,6 +99,29 @@ def recorded_traffic(workload, kernel):
     return rec.get("hbm_bytes_per_launch")
 
 
+class SpanTimer:
+    """Pairs of torch events (created up front by one record each) handed to
+    swg_time_next_call, so that a library call's kernels record them."""
+
+    def __init__(self, swg, n):
+        import torch
+        self.swg = swg
+        stream = torch.cuda.current_stream()
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+        for a, b in self.ev:
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+
+    def arm(self, i):
+        self.swg.swg_time_next_call(*self.ev[i])
+
+    def seconds(self, i):
+        a, b = self.ev[i]
+        return a.elapsed_time(b) * 1e-3
+
+
 def time_forward(swg, d, M, K, N, warmup, steps):
     """The SwiGLU forward entry point (g, fc, y from x, W, b) at the same shape, timed on
     its own after the step (it is not part of the backward step or of `value`)."""
@@ -101,25 +130,24 @@ def time_forward(swg, d, M, K, N, warmup, steps):
     args = (d["x"], d["w_g"], d["w_fc"], d["b_g"], d["b_fc"], g, fc, y)
     for _ in range(warmup):
         swg.swiglu_fwd(*args)
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    timer = SpanTimer(swg, steps)
+    for i in range(steps):
+        timer.arm(i)
         swg.swiglu_fwd(*args)
-    e1.record(stream)
     torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / steps
+    t = sum(timer.seconds(i) for i in range(steps)) / steps
     flops = 4.0 * M * K * N
     return {"us": round(t * 1e6, 2), "TFLOP/s": round(flops / t / 1e12, 1),
             "frac": round(flops / MFMA_BF16_PEAK / t, 4), "kernels": ["fwd_kernel"],
-            "note": "SwiGLU forward (g, fc, y), timed separately; not part of the step"}
+            "note": "SwiGLU forward (g, fc, y), mean kernel span, timed separately; not "
+                    "part of the step"}
 
 
 def time_swish_context(swg, steps):
     """The Swish gradient on the one workload the pages time: an fp16 [32, 64, 56, 56]
     activation with beta = 1 (Ascend C custom-operator page, performance table).  Each
     call is preceded by a 1 GiB write, so its inputs come from HBM and not from the
-    256 MB last-level cache; each call is bracketed by its own events.  Reported beside
+    256 MB last-level cache; each call is timed by its kernel span.  Reported beside
     the step, not part of `value`."""
     import torch
     from workloads.gen import SWISH_CONTEXT, swish_inputs
@@ -132,17 +160,15 @@ def time_swish_context(swg, steps):
            swish_inputs(c["dtype"], L=L, seed=c["seed"]).items()}
     out = torch.empty_like(inp["grad"])
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    timer = SpanTimer(swg, steps + 3)
     times = []
     for i in range(steps + 3):
         flush.fill_(i & 0xFF)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        timer.arm(i)
         swg.swish_grad(inp["grad"], inp["x"], grad_x=out, beta=c["beta"])
-        e1.record(stream)
-        e1.synchronize()
+        torch.cuda.synchronize()
         if i >= 3:
-            times.append(e0.elapsed_time(e1) * 1e-3)
+            times.append(timer.seconds(i))
     times.sort()
     t = times[len(times) // 2]
     nbytes = 3 * 2 * L
@@ -150,15 +176,15 @@ def time_swish_context(swg, steps):
             "median_us": round(t * 1e6, 2), "min_us": round(times[0] * 1e6, 2),
             "GB/s": round(nbytes / t / 1e9, 1), "frac": round(nbytes / HBM_PEAK / t, 4),
             "pages_us": {"ascend_c_kernel": 280, "autodiff": 420},
-            "note": "median of per-call events (launch overhead included) after a 1 GiB "
-                    "cache-evicting write; the pages' times are Ascend 910B, context only"}
+            "note": "median kernel span of one call after a 1 GiB cache-evicting write; "
+                    "the pages' times are Ascend 910B, context only"}
 
 
 def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
     """The b, w and x stages at the other SwiGLU workloads (same seeded recipe), each
     stage call preceded by a 1 GiB write that evicts the 256 MB last-level cache (the
-    tiny and ragged working sets would otherwise stay in it) and bracketed by its own
-    events, median over `steps` calls.  Reported beside the step (the tiny and ragged
+    tiny and ragged working sets would otherwise stay in it) and timed by its kernel span,
+    median over `steps` calls.  Reported beside the step (the tiny and ragged
     shapes are launch- and latency-bound; the LLM-sized FFN is matrix-core bound); not
     part of `value`."""
     import torch
@@ -190,20 +216,17 @@ def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
         for _ in range(warmup):
             for f in calls.values():
                 f()
-        ev = []
+        timer = SpanTimer(swg, steps * len(calls))
         for it in range(steps):
-            e = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in calls]
             for i, f in enumerate(calls.values()):
                 flush.fill_((it + i) & 0xFF)
-                e[i][0].record(stream)
+                timer.arm(it * len(calls) + i)
                 f()
-                e[i][1].record(stream)
-            ev.append(e)
         torch.cuda.synchronize()
         work = stage_work(M, K, N, 0)
         out = {"M": M, "K": K, "N": N}
         for i, st in enumerate(calls):
-            ts = sorted(e[i][0].elapsed_time(e[i][1]) * 1e-3 for e in ev)
+            ts = sorted(timer.seconds(it * len(calls) + i) for it in range(steps))
             t = ts[len(ts) // 2]
             wk = work[st]
             e = {"median_us": round(t * 1e6, 2), "frac": round(wk["t_roof"] / t, 4),
@@ -361,41 +384,46 @@ def main():
                        dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    names = ["b", "w", "x"] + [f"swish_grad_{dt}" for dt in SWISH_DTYPES]
     stream = torch.cuda.current_stream()
+    calls = [
+        ("b", lambda: swg.swiglu_bwd_b(d["dy"], d["g"], d["fc"], dg, dfc, db_g, db_fc,
+                                       workspace=ws_b)),
+        ("w", lambda: swg.swiglu_bwd_w(d["x"], dg, dfc, dw_g, dw_fc, workspace=ws_w)),
+        ("x", lambda: swg.swiglu_bwd_x(dg, dfc, d["w_g"], d["w_fc"], dx)),
+    ] + [(f"swish_grad_{dt}",
+          (lambda dt=dt: swg.swish_grad(sw[dt]["grad"], sw[dt]["x"], grad_x=sw_out[dt],
+                                        beta=SWISH_BETA)))
+         for dt in SWISH_DTYPES]
+    names = [n for n, _ in calls]
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        swg.swiglu_bwd_b(d["dy"], d["g"], d["fc"], dg, dfc, db_g, db_fc, workspace=ws_b)
-        if ev is not None:
-            ev[1].record(stream)
-        swg.swiglu_bwd_w(d["x"], dg, dfc, dw_g, dw_fc, workspace=ws_w)
-        if ev is not None:
-            ev[2].record(stream)
-        swg.swiglu_bwd_x(dg, dfc, d["w_g"], d["w_fc"], dx)
-        if ev is not None:
-            ev[3].record(stream)
-        for i, dt in enumerate(SWISH_DTYPES):
-            swg.swish_grad(sw[dt]["grad"], sw[dt]["x"], grad_x=sw_out[dt], beta=SWISH_BETA)
-            if ev is not None:
-                ev[4 + i].record(stream)
+    def step(s=None):
+        for i, (_, f) in enumerate(calls):
+            if s is not None:
+                events[s][i].record(stream)
+                spans.arm(s * len(calls) + i)
+            f()
+        if s is not None:
+            events[s][len(calls)].record(stream)
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
               for _ in range(args.steps)]
+    spans = SpanTimer(swg, args.steps * len(calls))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(events[s])
+        step(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    samples = {n: [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for ev in events]
+    samples = {n: [spans.seconds(s * len(calls) + i) for s in range(args.steps)]
                for i, n in enumerate(names)}
+    around = {n: [ev[i].elapsed_time(ev[i + 1]) * 1e-3 for ev in events]
+              for i, n in enumerate(names)}
     per_stage = {n: sum(v) / len(v) for n, v in samples.items()}
     step_s = sum(per_stage.values())
+    event_step_s = sum(sum(v) / len(v) for v in around.values())
     work = stage_work(M, K, N, L)
     t_roof = sum(v["t_roof"] for v in work.values())
 
@@ -407,6 +435,7 @@ def main():
         e = {"us": round(t * 1e6, 2),
              "median_us": round(srt[len(srt) // 2] * 1e6, 2),
              "min_us": round(srt[0] * 1e6, 2), "max_us": round(srt[-1] * 1e6, 2),
+             "event_us": round(sum(around[n]) / len(around[n]) * 1e6, 2),
              "GB/s": round(wk["bytes"] / t / 1e9, 1),
              "bound": wk["bound"], "roofline_us": round(wk["t_roof"] * 1e6, 2),
              "frac": round(wk["t_roof"] / t, 4),
@@ -444,7 +473,11 @@ def main():
         "config": {"workload": f"swiglu_bwd {shape.name} M={M} K={K} N={N} bf16 + swish_grad "
                                f"L={L} fp32/fp16/bf16 beta={SWISH_BETA}",
                    "M": M, "K": K, "N": N, "swish_L": L, "parallelism": "single GPU"},
-        "event_ms_per_step": round(step_s * 1e3, 4),
+        "kernel_ms_per_step": round(step_s * 1e3, 4),
+        "event_ms_per_step": round(event_step_s * 1e3, 4),
+        "timing": "stage us = mean kernel span per call (HIP events attached to the call's "
+                  "first and last kernel dispatch with swg_time_next_call); event_us = events "
+                  "recorded around the call; value = 100 * roofline time / kernel time",
         "roofline_ms_per_step": round(t_roof * 1e3, 4),
         "stages": stages,
         "roofline": roof,

@@ -31,7 +31,9 @@
  *     matching *_workspace_size query.  SWG_ERR_HIP means a launch failed; the HIP error
  *     code is then available from swg_last_hip_error().  Calls whose work is empty return
  *     SWG_OK without launching anything.
- *   - Calls are thread-safe: the library keeps no state apart from the last HIP error.
+ *   - Calls are thread-safe: the library keeps no state apart from the last HIP error, the
+ *     timing events of swg_time_next_call (both per host thread) and the device scratch
+ *     of swiglu_bwd_b_noalloc.
  */
 #ifndef SWIGLU_BWD_H
 #define SWIGLU_BWD_H
@@ -183,6 +185,19 @@ swg_status swish_grad_strided(const void* grad, const void* x, void* grad_x, int
                               const int64_t* sizes, const int64_t* grad_strides,
                               const int64_t* x_strides, const int64_t* out_strides,
                               swg_dtype dtype, const float* beta, void* stream);
+
+/*
+ * Kernel-duration timing for measurement harnesses.  The next entry-point call made on
+ * the calling thread dispatches its kernels with these two events attached
+ * (hipExtLaunchKernel): `start_event` is recorded when its first kernel begins and
+ * `stop_event` when its last kernel ends, so hipEventElapsedTime(start, stop) after that
+ * call is the span of its kernels on the GPU, without the dispatch gaps that events
+ * recorded around the call include.  Both are hipEvent_t handles created by the caller
+ * (timing enabled) on the device of the call; both NULL cancels.  The setting applies to
+ * that one call and is cleared when it returns; a call that launches nothing (empty
+ * input, argument error) records neither event.  SWG_ERR_INVALID if only one is NULL.
+ */
+swg_status swg_time_next_call(void* start_event, void* stop_event);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* swg_status_string(int status);

@@ -16,6 +16,7 @@ import torch
 __all__ = ["SwgError", "load_library", "library_path", "swish_grad", "swish_grad_strided",
            "swiglu_bwd_b", "swiglu_bwd_b_noalloc", "swiglu_bwd_w", "swiglu_bwd_x", "swiglu_fwd",
            "swiglu_bwd_b_workspace_size", "swiglu_bwd_w_workspace_size", "swg_version",
+           "swg_time_next_call",
            "DTYPE_CODE", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +80,8 @@ def load_library():
         lib.swg_status_string.restype = ctypes.c_char_p
         lib.swg_last_hip_error.argtypes = []
         lib.swg_last_hip_error.restype = i32
+        lib.swg_time_next_call.argtypes = [vp, vp]
+        lib.swg_time_next_call.restype = i32
         lib.swg_version.argtypes = []
         lib.swg_version.restype = ctypes.c_char_p
         _lib = lib
@@ -157,6 +160,24 @@ def _workspace(nbytes, workspace, device, stream):
 
 def swg_version() -> str:
     return load_library().swg_version().decode()
+
+
+def swg_time_next_call(start, stop):
+    """Attach two ``torch.cuda.Event`` (timing enabled, each recorded at least once so that
+    torch has created it) to the kernels of the next library call on this thread: after it,
+    ``start.elapsed_time(stop)`` is the span from its first kernel's start to its last
+    kernel's end.  ``None, None`` cancels."""
+    lib = load_library()
+    handles = []
+    for name, e in (("start", start), ("stop", stop)):
+        if e is None:
+            handles.append(None)
+            continue
+        h = e.cuda_event
+        if not h:
+            raise ValueError(f"{name} event has no HIP event yet: record it once first")
+        handles.append(ctypes.c_void_p(h))
+    _check("swg_time_next_call", lib.swg_time_next_call(*handles), lib)
 
 
 def _same_kind(name, t, dtype, shape, device):

@@ -31,6 +31,13 @@ swg_status hip_status(hipError_t e) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+thread_local swg::CallTiming g_timing;
+
+// Clears the timing events when an entry point returns (they time one call only).
+struct TimedCall {
+  ~TimedCall() { g_timing = swg::CallTiming{}; }
+};
+
 // A buffer as a byte range [p, p + bytes); bytes = 0 marks an absent buffer.
 struct Span {
   const void* p;
@@ -94,7 +101,16 @@ int gemm_grid_cap() {
 
 }  // namespace
 
+swg::CallTiming& swg::call_timing() { return g_timing; }
+
 extern "C" {
+
+swg_status swg_time_next_call(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return SWG_ERR_INVALID;
+  g_timing.start = reinterpret_cast<hipEvent_t>(start_event);
+  g_timing.stop = reinterpret_cast<hipEvent_t>(stop_event);
+  return SWG_OK;
+}
 
 const char* swg_version(void) { return "swiglu_bwd 0.1.0 gfx950"; }
 
@@ -115,6 +131,7 @@ int swg_last_hip_error(void) { return g_last_hip_error; }
 // ------------------------------------------------------------------- swish_grad
 swg_status swish_grad(const void* grad, const void* x, void* grad_x, int64_t n, swg_dtype dtype,
                       const float* beta, void* stream) {
+  TimedCall timed_;
   if (!dtype_ok(dtype) || n < 0) return SWG_ERR_INVALID;
   if (n == 0) return SWG_OK;
   if (grad == nullptr || x == nullptr || grad_x == nullptr) return SWG_ERR_NULLPTR;
@@ -137,6 +154,7 @@ swg_status swish_grad_strided(const void* grad, const void* x, void* grad_x, int
                               const int64_t* sizes, const int64_t* grad_strides,
                               const int64_t* x_strides, const int64_t* out_strides,
                               swg_dtype dtype, const float* beta, void* stream) {
+  TimedCall timed_;
   if (!dtype_ok(dtype) || ndim < 0 || ndim > SWG_MAX_NDIM) return SWG_ERR_INVALID;
   if (ndim > 0 && (!sizes || !grad_strides || !x_strides || !out_strides))
     return SWG_ERR_NULLPTR;
@@ -291,6 +309,7 @@ static swg_status b_checks(const void* dy, const void* g, const void* fc, void* 
 swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc, void* dg, void* dfc,
                         void* db_g, void* db_fc, int64_t M, int64_t N, swg_dtype dtype,
                         void* workspace, size_t workspace_bytes, void* stream) {
+  TimedCall timed_;
   BPlan p{};
   const swg_status st = b_checks(dy, g, fc, dg, dfc, db_g, db_fc, M, N, dtype, workspace,
                                  workspace_bytes, true, &p);
@@ -302,6 +321,7 @@ swg_status swiglu_bwd_b(const void* dy, const void* g, const void* fc, void* dg,
 swg_status swiglu_bwd_b_noalloc(const void* dy, const void* g, const void* fc, void* dg,
                                 void* dfc, void* db_g, void* db_fc, int64_t M, int64_t N,
                                 swg_dtype dtype, void* stream) {
+  TimedCall timed_;
   BPlan p{};
   const swg_status st = b_checks(dy, g, fc, dg, dfc, db_g, db_fc, M, N, dtype, nullptr, 0,
                                  false, &p);
@@ -337,6 +357,7 @@ size_t swiglu_bwd_w_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dt
 swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc, void* dw_g, void* dw_fc,
                         int64_t M, int64_t K, int64_t N, swg_dtype dtype, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  TimedCall timed_;
   swg_status st = gemm_shape_check(dtype, M, K, N, true);
   if (st != SWG_OK) return st;
   if (M == 0 || K == 0 || N == 0) return SWG_OK;  // dw += empty sum
@@ -361,6 +382,7 @@ swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc, void* dw
 
 swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
                         void* dx, int64_t M, int64_t K, int64_t N, swg_dtype dtype, void* stream) {
+  TimedCall timed_;
   swg_status st = gemm_shape_check(dtype, M, K, N, true);
   if (st != SWG_OK) return st;
   if (M == 0 || K == 0) return SWG_OK;  // dx is empty
@@ -386,6 +408,7 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
 swg_status swiglu_fwd(const void* x, const void* w_g, const void* w_fc, const void* b_g,
                       const void* b_fc, void* g, void* fc, void* y, int64_t M, int64_t K,
                       int64_t N, swg_dtype dtype, void* stream) {
+  TimedCall timed_;
   swg_status st = gemm_shape_check(dtype, M, K, N, true);
   if (st != SWG_OK) return st;
   if (M == 0 || N == 0) return SWG_OK;  // outputs are empty

@@ -117,12 +117,12 @@ static hipError_t swish_grad_t(const void* grad, const void* x, void* out, int64
     int64_t blocks = ceil_div(nvec, 256 * U);
     if (blocks > kMaxBlocks) blocks = kMaxBlocks;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((swish_grad_vec_kernel<T, U>), dim3((unsigned)blocks), dim3(256), 0,
+    SWG_LAUNCH((swish_grad_vec_kernel<T, U>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, g, xx, o, n, beta);
   } else {
     int64_t blocks = ceil_div(n, 256);
     if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
-    hipLaunchKernelGGL((swish_grad_scalar_kernel<T>), dim3((unsigned)blocks), dim3(256), 0,
+    SWG_LAUNCH((swish_grad_scalar_kernel<T>), dim3((unsigned)blocks), dim3(256), 0,
                        stream, g, xx, o, n, beta);
   }
   return hipGetLastError();
@@ -303,17 +303,17 @@ static hipError_t b_stage_t(const BPlan& p, const void* dy, const void* g, const
   const T* b = static_cast<const T*>(g);
   const T* c = static_cast<const T*>(fc);
   if (p.vec > 1) {
-    hipLaunchKernelGGL((b_stage_kernel<T, true, kBRowsInFlight>), grid, dim3(256), 0, stream, a, b, c,
+    SWG_LAUNCH((b_stage_kernel<T, true, kBRowsInFlight>), grid, dim3(256), 0, stream, a, b, c,
                        static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.unit_rows,
                        p.nunits, txlog2);
   } else {
-    hipLaunchKernelGGL((b_stage_kernel<T, false, 1>), grid, dim3(256), 0, stream, a, b, c,
+    SWG_LAUNCH((b_stage_kernel<T, false, 1>), grid, dim3(256), 0, stream, a, b, c,
                        static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.unit_rows,
                        p.nunits, txlog2);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((db_finalize_kernel<T>), dim3((unsigned)ceil_div(2 * N, 16)), dim3(256), 0,
+  SWG_LAUNCH((db_finalize_kernel<T>), dim3((unsigned)ceil_div(2 * N, 16)), dim3(256), 0,
                      stream, part, static_cast<T*>(db_g), static_cast<T*>(db_fc), N, p.nwalk);
   return hipGetLastError();
 }

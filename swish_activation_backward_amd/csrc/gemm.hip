@@ -1222,12 +1222,12 @@ static hipError_t x_stage_t(const void* dg, const void* dfc, const void* wg, con
   // per-lane column tests unless every double stage is whole: N a multiple of 64 and at
   // least two double stages per half (N = 64 pads the half with a stage past N)
   if (N % XA_BR == 0 && N >= 2 * XA_BR)
-    hipLaunchKernelGGL((x_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+    SWG_LAUNCH((x_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        static_cast<const T*>(dg), static_cast<const T*>(dfc),
                        static_cast<const T*>(wg), static_cast<const T*>(wfc),
                        static_cast<T*>(dx), M, K, N, nq, ntiles);
   else
-    hipLaunchKernelGGL((x_stage_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
+    SWG_LAUNCH((x_stage_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        static_cast<const T*>(dg), static_cast<const T*>(dfc),
                        static_cast<const T*>(wg), static_cast<const T*>(wfc),
                        static_cast<T*>(dx), M, K, N, nq, ntiles);
@@ -1251,12 +1251,12 @@ static hipError_t w_stage_t(const WPlan& p, const void* x, const void* dg, const
   const int64_t grid = nitems < cus ? nitems : cus;
   // per-lane column tests only for tiles cut by the right or bottom edge of dW
   if (K % BP == 0 && N % BQ == 0)
-    hipLaunchKernelGGL((w_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+    SWG_LAUNCH((w_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        static_cast<const T*>(x), static_cast<const T*>(dg),
                        static_cast<const T*>(dfc), static_cast<T*>(dwg), static_cast<T*>(dwfc),
                        wsp, M, K, N, p.tn / 2, p.tiles, p.rows, nitems);
   else
-    hipLaunchKernelGGL((w_stage_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
+    SWG_LAUNCH((w_stage_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        static_cast<const T*>(x), static_cast<const T*>(dg),
                        static_cast<const T*>(dfc), static_cast<T*>(dwg), static_cast<T*>(dwfc),
                        wsp, M, K, N, p.tn / 2, p.tiles, p.rows, nitems);
@@ -1264,7 +1264,7 @@ static hipError_t w_stage_t(const WPlan& p, const void* x, const void* dg, const
   if (e != hipSuccess || p.splits == 1) return e;
   int64_t blocks = ceil_div(K * 2 * N / 4, 256);
   if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
-  hipLaunchKernelGGL((w_reduce_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, stream, ws,
+  SWG_LAUNCH((w_reduce_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, stream, ws,
                      static_cast<T*>(dwg), static_cast<T*>(dwfc), K, N, p.splits);
   return hipGetLastError();
 }
@@ -1279,7 +1279,7 @@ hipError_t launch_w_stage(int dtype, const WPlan& p, const void* x, const void* 
   if (e != hipSuccess || p.splits == 1) return e;
   int64_t blocks = ceil_div(K * 2 * N / 4, 256);
   if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
-  hipLaunchKernelGGL((w_reduce_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, stream, ws,
+  SWG_LAUNCH((w_reduce_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, stream, ws,
                      static_cast<float*>(dw_g), static_cast<float*>(dw_fc), K, N, p.splits);
   return hipGetLastError();
 }
@@ -1294,13 +1294,13 @@ static hipError_t fwd_t(const void* x, const void* wg, const void* wfc, const vo
   // per-lane column tests unless every stage is whole: K a multiple of a ring round
   // (stages past K would otherwise read the next row of x) and N of the tile width
   if (K % (4 * BR) == 0 && N % FN == 0)
-    hipLaunchKernelGGL((fwd_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+    SWG_LAUNCH((fwd_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        static_cast<const T*>(x), static_cast<const T*>(wg),
                        static_cast<const T*>(wfc), static_cast<const T*>(bg),
                        static_cast<const T*>(bfc), static_cast<T*>(g), static_cast<T*>(fc),
                        static_cast<T*>(y), M, K, N, nn, ntiles);
   else
-    hipLaunchKernelGGL((fwd_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
+    SWG_LAUNCH((fwd_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        static_cast<const T*>(x), static_cast<const T*>(wg),
                        static_cast<const T*>(wfc), static_cast<const T*>(bg),
                        static_cast<const T*>(bfc), static_cast<T*>(g), static_cast<T*>(fc),
@@ -1321,7 +1321,7 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
   int64_t blocks = ceil_div(words, 256);
   if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+  SWG_LAUNCH(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<uint32_t*>(p), words);
   return hipGetLastError();
 }

@@ -262,7 +262,7 @@ hipError_t launch_fwd32(const void* x, const void* w_g, const void* w_fc, const 
                         const void* b_fc, void* g, void* fc, void* y, int64_t M, int64_t K,
                         int64_t N, hipStream_t stream) {
   const int64_t np = ceil_div(M, T32), nn = ceil_div(N, T32);
-  hipLaunchKernelGGL(fwd32_kernel, dim3((unsigned)(np * nn)), dim3(NT32), 0, stream,
+  SWG_LAUNCH(fwd32_kernel, dim3((unsigned)(np * nn)), dim3(NT32), 0, stream,
                      static_cast<const float*>(x), static_cast<const float*>(w_g),
                      static_cast<const float*>(w_fc), static_cast<const float*>(b_g),
                      static_cast<const float*>(b_fc), static_cast<float*>(g),
@@ -273,7 +273,7 @@ hipError_t launch_fwd32(const void* x, const void* w_g, const void* w_fc, const 
 hipError_t launch_x_stage32(const void* dg, const void* dfc, const void* w_g, const void* w_fc,
                             void* dx, int64_t M, int64_t K, int64_t N, hipStream_t stream) {
   const int64_t np = ceil_div(M, T32), nq = ceil_div(K, T32);
-  hipLaunchKernelGGL(x_stage32_kernel, dim3((unsigned)(np * nq)), dim3(NT32), 0, stream,
+  SWG_LAUNCH(x_stage32_kernel, dim3((unsigned)(np * nq)), dim3(NT32), 0, stream,
                      static_cast<const float*>(dg), static_cast<const float*>(dfc),
                      static_cast<const float*>(w_g), static_cast<const float*>(w_fc),
                      static_cast<float*>(dx), M, K, N, nq);
@@ -286,7 +286,7 @@ hipError_t launch_w_stage32(const WPlan& p, const void* x, const void* dg, const
   const int64_t tk = ceil_div(K, T32), tnh = ceil_div(N, T32);
   const int64_t items = p.splits * tk * 2 * tnh;
   float* wsp = p.splits > 1 ? ws : nullptr;
-  hipLaunchKernelGGL(w_stage32_kernel, dim3((unsigned)items), dim3(NT32), 0, stream,
+  SWG_LAUNCH(w_stage32_kernel, dim3((unsigned)items), dim3(NT32), 0, stream,
                      static_cast<const float*>(x), static_cast<const float*>(dg),
                      static_cast<const float*>(dfc), static_cast<float*>(dw_g),
                      static_cast<float*>(dw_fc), wsp, M, K, N, tk, tnh, p.rows);

@@ -1,12 +1,37 @@
 // Internal launchers (C++ linkage) called by the C ABI layer after validation.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "plan.hpp"
 
 namespace swg {
+
+// Kernel-duration timing of one entry-point call (swg_time_next_call): caller-created HIP
+// events, per host thread, cleared when the timed call returns.
+struct CallTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+CallTiming& call_timing();
+
+// Every kernel of the library is dispatched through this.  While a call is timed, the
+// dispatch carries the call's events (hipExtLaunchKernelGGL): the first dispatch records
+// `start` when it begins and every dispatch records `stop` when it ends, so the pair spans
+// the call's kernels from the first one's start to the last one's end.
+#define SWG_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                 \
+  do {                                                                                    \
+    ::swg::CallTiming& t_ = ::swg::call_timing();                                         \
+    if (t_.stop == nullptr) {                                                             \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                 \
+    } else {                                                                              \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, t_.start, t_.stop, 0,       \
+                            __VA_ARGS__);                                                 \
+      t_.start = nullptr;                                                                 \
+    }                                                                                     \
+  } while (0)
 
 constexpr int64_t kMaxStreamBlocks = 8192;
 

@@ -242,13 +242,13 @@ static hipError_t swish_grad_strided_t(const void* grad, const void* x, void* ou
     if (line4_ok(grad, v.stride[0][0], v.stride[0][1], es) &&
         line4_ok(x, v.stride[1][0], v.stride[1][1], es) &&
         line4_ok(out, v.stride[2][0], v.stride[2][1], es)) {
-      hipLaunchKernelGGL((swish_grad_tr2d_vec_kernel<T>), dim3((unsigned)tiles), dim3(256), 0,
+      SWG_LAUNCH((swish_grad_tr2d_vec_kernel<T>), dim3((unsigned)tiles), dim3(256), 0,
                          stream, static_cast<const T*>(grad), static_cast<const T*>(x),
                          static_cast<T*>(out), R, C, v.stride[0][0], v.stride[0][1],
                          v.stride[1][0], v.stride[1][1], v.stride[2][0], v.stride[2][1], beta);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((swish_grad_tr2d_kernel<T>), dim3((unsigned)tiles), dim3(256), 0, stream,
+    SWG_LAUNCH((swish_grad_tr2d_kernel<T>), dim3((unsigned)tiles), dim3(256), 0, stream,
                        static_cast<const T*>(grad), static_cast<const T*>(x),
                        static_cast<T*>(out), R, C, v.stride[0][0], v.stride[0][1],
                        v.stride[1][0], v.stride[1][1], v.stride[2][0], v.stride[2][1], beta);
@@ -274,10 +274,10 @@ static hipError_t swish_grad_strided_t(const void* grad, const void* x, void* ou
   const T* xx = static_cast<const T*>(x);
   T* o = static_cast<T*>(out);
   if (narrow)
-    hipLaunchKernelGGL((swish_grad_strided_kernel<T, false>), dim3((unsigned)blocks), dim3(256),
+    SWG_LAUNCH((swish_grad_strided_kernel<T, false>), dim3((unsigned)blocks), dim3(256),
                        0, stream, g, xx, o, a, n, beta);
   else
-    hipLaunchKernelGGL((swish_grad_strided_kernel<T, true>), dim3((unsigned)blocks), dim3(256),
+    SWG_LAUNCH((swish_grad_strided_kernel<T, true>), dim3((unsigned)blocks), dim3(256),
                        0, stream, g, xx, o, a, n, beta);
   return hipGetLastError();
 }

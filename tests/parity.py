@@ -12,7 +12,9 @@ Three checks are applied to every output tensor:
    rounding model of the arithmetic that produced the value (fp32 math + one final
    rounding).  This binds where atol = 1e-4 exceeds the outputs themselves;
 3. a normwise bound ||gpu - ref||_2 <= nw * ||ref||_2 (bf16: 2^-8, the unit roundoff of
-   an 8-bit significand; a correctly rounded bf16 tensor sits near 0.4 * 2^-8).
+   an 8-bit significand; a correctly rounded bf16 tensor sits near 0.4 * 2^-8), plus
+   sqrt(n) * 2^-25 for fp16, whose subnormals (below 2^-14) are spaced 2^-24 apart so that
+   a correctly rounded value may miss by half of that whatever its size.
 
 ``Checker`` accumulates the three over chunks so that large tensors can be compared
 piecewise; ``compare`` is the one-shot form.
@@ -148,7 +150,8 @@ class Checker:
     def result(self, raise_on_fail=True):
         nr, ne = np.sqrt(self.ss_ref), np.sqrt(self.ss_err)
         normwise = ne / nr if nr > 0 else ne
-        normwise_bad = (ne > self.nw * nr) if nr > 0 else (ne > 0)
+        floor = np.sqrt(self.n) * FP16_SUBNORMAL_HALF if self.dtype == "fp16" else 0.0
+        normwise_bad = (ne > self.nw * nr + floor) if nr > 0 else (ne > floor)
         stats = {"name": self.name, "n": self.n, "nonfinite": self.nonfinite,
                  "contract_fail": self.contract_fail, "mixed_fail": self.mixed_fail,
                  "normwise": float(normwise), "normwise_fail": bool(normwise_bad),

@@ -55,6 +55,16 @@ def test_status_strings_and_version(lib):
     assert lib.swg_last_hip_error() == 0
 
 
+def test_time_next_call_arguments(lib):
+    assert lib.swg_time_next_call(NULL, NULL) == OK      # cancels
+    assert lib.swg_time_next_call(P, NULL) == INVALID
+    assert lib.swg_time_next_call(NULL, Q) == INVALID
+    # an argument error in the next call returns before any launch and clears the events
+    assert lib.swg_time_next_call(P, Q) == OK
+    assert lib.swish_grad(P, Q, R, -1, BF16, None, NULL) == INVALID
+    assert lib.swish_grad(P, Q, R, 0, BF16, None, NULL) == OK
+
+
 def test_swish_grad_argument_errors(lib):
     beta = ctypes.byref(ctypes.c_float(1.0))
     assert lib.swish_grad(P, Q, R, 0, BF16, beta, NULL) == OK          # empty: no work

@@ -44,3 +44,6 @@ def test_bench_json_line_on_the_tiny_workload():
     for name in ("b", "w", "x", "swish_grad_fp32", "swish_grad_fp16", "swish_grad_bf16"):
         st = d["stages"][name]
         assert st["us"] > 0 and 0 < st["frac"] <= 1, (name, st)
+        # the kernel span lies inside the events recorded around the call
+        assert st["us"] <= st["event_us"] + 5.0, (name, st)
+    assert abs(roof["avg_launch_us"] - d["stages"][roof["stage"]]["us"]) < 0.01
