@@ -143,6 +143,39 @@ def time_forward(swg, d, M, K, N, warmup, steps):
                     "part of the step"}
 
 
+def time_fused(swg, d, dg, dfc, M, K, N, warmup, steps):
+    """The fused w + x pass (swiglu_bwd_wx: dW and dx in one launch over [dg | dfc]) on the
+    step's inputs, timed on its own beside the unfused w and x stages (not part of the
+    step or of `value`).  Algorithmic work: the two GEMMs' flops; bytes x, [dg | dfc] and
+    W read once, dx written, dW read and written."""
+    import torch
+    dev = d["x"].device
+    dw_g = torch.zeros(K, N, dtype=torch.bfloat16, device=dev)
+    dw_fc = torch.zeros_like(dw_g)
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, swg.swiglu_bwd_wx_workspace_size(M, K, N, torch.bfloat16)),
+                     dtype=torch.uint8, device=dev)
+    args = (d["x"], dg, dfc, d["w_g"], d["w_fc"], dw_g, dw_fc, dx)
+    for _ in range(warmup):
+        swg.swiglu_bwd_wx(*args, workspace=ws)
+    timer = SpanTimer(swg, steps)
+    for i in range(steps):
+        timer.arm(i)
+        swg.swiglu_bwd_wx(*args, workspace=ws)
+    torch.cuda.synchronize()
+    ts = sorted(timer.seconds(i) for i in range(steps))
+    t = sum(ts) / steps
+    flops = 8.0 * M * K * N
+    nbytes = 2 * M * K + 4 * M * N + 4 * K * N + 2 * M * K + 8 * K * N
+    return {"us": round(t * 1e6, 2), "median_us": round(ts[len(ts) // 2] * 1e6, 2),
+            "min_us": round(ts[0] * 1e6, 2), "TFLOP/s": round(flops / t / 1e12, 1),
+            "GB/s": round(nbytes / t / 1e9, 1), "bound": "mfma",
+            "frac": round(flops / MFMA_BF16_PEAK / t, 4),
+            "kernels": ["wx_fused_kernel", "w_reduce_kernel"],
+            "note": "fused w + x pass (swiglu_bwd_wx), mean kernel span on the step's "
+                    "inputs; compare with stages w + x; not part of the step"}
+
+
 def time_swish_context(swg, steps):
     """The Swish gradient on the one workload the pages time: an fp16 [32, 64, 56, 56]
     activation with beta = 1 (Ascend C custom-operator page, performance table).  Each
@@ -488,6 +521,8 @@ def main():
     for n in names:
         if stages[n]["bound"] == "hbm":
             stages[n]["frac_of_copy"] = round(work[n]["bytes"] / per_stage[n] / copy_rate, 4)
+    out["fused_wx"] = time_fused(swg, d, dg, dfc, M, K, N, args.warmup, args.steps)
+    out["fused_wx"]["unfused_w_plus_x_us"] = round(stages["w"]["us"] + stages["x"]["us"], 2)
     out["forward"] = time_forward(swg, d, M, K, N, args.warmup, args.steps)
     out["swish_pages_shape"] = time_swish_context(swg, 20)
     if not args.no_per_config:

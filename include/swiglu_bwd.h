@@ -134,6 +134,31 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
                         void* stream);
 
 /*
+ * Fused w + x pass [SwiGLU page, formulas 3 and 4, which contract the same [dg | dfc], and
+ * the operator background's motive for fusion: intermediates should not make repeated
+ * trips through memory]: the results of swiglu_bwd_w followed by swiglu_bwd_x from one
+ * kernel launch (plus, when M is split, the in-order reduction of the fp32 partials):
+ *   [dw_g | dw_fc] += x^T [dg | dfc]   (accumulated, one rounding, as swiglu_bwd_w)
+ *   dx = [dg | dfc] [W_g | W_fc]^T     (overwritten, as swiglu_bwd_x)
+ * Half of the workgroups compute dx tiles row block after row block while the other half
+ * compute dW tiles over 256-row chunks of [dg | dfc] taken round-robin by S splits, so
+ * that both halves read the same rows at about the same time and [dg | dfc] crosses HBM
+ * about once (the separate calls read it twice).  dx is bit-identical to swiglu_bwd_x;
+ * dW groups its fp32 partial sums by chunk and may differ from swiglu_bwd_w in the last
+ * bit.  dtype bf16 or fp16 (fp32: SWG_ERR_UNSUPPORTED); the shape and alignment rules of
+ * swiglu_bwd_w and swiglu_bwd_x; dx, dw_g, dw_fc and the workspace may not overlap each
+ * other or an input (SWG_ERR_INVALID).  `workspace`: swiglu_bwd_wx_workspace_size(M, K, N,
+ * dtype) bytes (S * K * 2N fp32 partials; 0 when S = 1).  N = 0 writes dx = 0 (the
+ * inputs and dW, all empty, may then be NULL).
+ */
+swg_status swiglu_bwd_wx(const void* x, const void* dg, const void* dfc,
+                         const void* w_g, const void* w_fc,
+                         void* dw_g, void* dw_fc, void* dx,
+                         int64_t M, int64_t K, int64_t N, swg_dtype dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+size_t swiglu_bwd_wx_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dtype);
+
+/*
  * SwiGLU forward [SwiGLU page, operator background: the function the three stages above
  * differentiate]:
  *   g[m,n]  = sum_k x[m,k] W_g[k,n]  + b_g[n]

@@ -7,7 +7,8 @@ binding loads the library lazily on first use and raises if it is missing.
 from ._lib import (  # noqa: F401
     DTYPE_CODE, STATUS, SwgError, library_path, load_library, swg_version, swiglu_bwd_b,
     swiglu_bwd_b_noalloc, swiglu_bwd_b_workspace_size, swiglu_bwd_w, swiglu_bwd_w_workspace_size, swiglu_bwd_x,
-    swiglu_fwd, swish_grad, swish_grad_strided, swg_time_next_call,
+    swiglu_bwd_wx, swiglu_bwd_wx_workspace_size, swiglu_fwd, swish_grad, swish_grad_strided,
+    swg_time_next_call,
 )
 
 __version__ = "0.1.0"

@@ -16,7 +16,7 @@ import torch
 __all__ = ["SwgError", "load_library", "library_path", "swish_grad", "swish_grad_strided",
            "swiglu_bwd_b", "swiglu_bwd_b_noalloc", "swiglu_bwd_w", "swiglu_bwd_x", "swiglu_fwd",
            "swiglu_bwd_b_workspace_size", "swiglu_bwd_w_workspace_size", "swg_version",
-           "swg_time_next_call",
+           "swg_time_next_call", "swiglu_bwd_wx", "swiglu_bwd_wx_workspace_size",
            "DTYPE_CODE", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +74,11 @@ def load_library():
         lib.swiglu_bwd_w_workspace_size.restype = sz
         lib.swiglu_bwd_x.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
         lib.swiglu_bwd_x.restype = i32
+        lib.swiglu_bwd_wx.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp,
+                                      sz, vp]
+        lib.swiglu_bwd_wx.restype = i32
+        lib.swiglu_bwd_wx_workspace_size.argtypes = [i64, i64, i64, i32]
+        lib.swiglu_bwd_wx_workspace_size.restype = sz
         lib.swiglu_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
         lib.swiglu_fwd.restype = i32
         lib.swg_status_string.argtypes = [i32]
@@ -322,6 +327,36 @@ def swiglu_bwd_x(dg, dfc, w_g, w_fc, dx, stream=None):
         st = lib.swiglu_bwd_x(_ptr(dg), _ptr(dfc), _ptr(w_g), _ptr(w_fc), _ptr(dx), M, K, N,
                               _dtype_code(dg), _stream(stream, dev))
     _check("swiglu_bwd_x", st, lib)
+
+
+def swiglu_bwd_wx_workspace_size(M: int, K: int, N: int, dtype) -> int:
+    return int(load_library().swiglu_bwd_wx_workspace_size(M, K, N, DTYPE_CODE[dtype]))
+
+
+def swiglu_bwd_wx(x, dg, dfc, w_g, w_fc, dw_g, dw_fc, dx, workspace=None, stream=None):
+    """Fused w + x pass: [dw_g | dw_fc] += x^T [dg | dfc] and dx = [dg | dfc] [W_g | W_fc]^T
+    (overwritten) in one launch over [dg | dfc]."""
+    lib = load_library()
+    if x.dim() != 2 or dg.dim() != 2 or w_g.dim() != 2:
+        raise ValueError("x must be [M, K], dg [M, N] and w_g [K, N]")
+    M, K = x.shape
+    N = dg.shape[1]
+    dt, dev = x.dtype, x.device
+    _dense("x", x, dt, (M, K), dev)
+    for name, t in (("dg", dg), ("dfc", dfc)):
+        _dense(name, t, dt, (M, N), dev)
+    for name, t in (("w_g", w_g), ("w_fc", w_fc), ("dw_g", dw_g), ("dw_fc", dw_fc)):
+        _dense(name, t, dt, (K, N), dev)
+    _dense("dx", dx, dt, (M, K), dev)
+    code = _dtype_code(x)
+    nbytes = int(lib.swiglu_bwd_wx_workspace_size(M, K, N, code))
+    with _on_device(dev):
+        ws = _workspace(nbytes, workspace, dev, stream)
+        st = lib.swiglu_bwd_wx(_ptr(x), _ptr(dg), _ptr(dfc), _ptr(w_g), _ptr(w_fc), _ptr(dw_g),
+                               _ptr(dw_fc), _ptr(dx), M, K, N, code, _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream, dev))
+    _check("swiglu_bwd_wx", st, lib)
 
 
 def swiglu_fwd(x, w_g, w_fc, b_g, b_fc, g, fc, y, stream=None):

@@ -404,6 +404,46 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
                                    as_stream(stream)));
 }
 
+// ------------------------------------------------------------------- fused w + x
+size_t swiglu_bwd_wx_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dtype) {
+  if (dtype == SWG_FP32 || gemm_shape_check(dtype, M, K, N) != SWG_OK || M == 0 || K == 0 ||
+      N == 0)
+    return 0;
+  return plan_wx(M, K, N).ws_bytes;
+}
+
+swg_status swiglu_bwd_wx(const void* x, const void* dg, const void* dfc, const void* w_g,
+                         const void* w_fc, void* dw_g, void* dw_fc, void* dx, int64_t M,
+                         int64_t K, int64_t N, swg_dtype dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  TimedCall timed_;
+  swg_status st = gemm_shape_check(dtype, M, K, N);   // bf16 / fp16 only
+  if (st != SWG_OK) return st;
+  if (M == 0 || K == 0) return SWG_OK;   // dx and dW are empty
+  if (!dx) return SWG_ERR_NULLPTR;
+  if (!aligned(dx, 16)) return SWG_ERR_UNSUPPORTED;
+  const int64_t es = elem_size(dtype);
+  if (N == 0)   // dx = 0 (the empty sum); dW is empty
+    return hip_status(launch_zero(dx, (size_t)M * (size_t)K * (size_t)es, as_stream(stream)));
+  if (!x || !dg || !dfc || !w_g || !w_fc || !dw_g || !dw_fc) return SWG_ERR_NULLPTR;
+  for (const void* p : {(const void*)dw_g, (const void*)dw_fc})
+    if (!aligned(p, 8)) return SWG_ERR_UNSUPPORTED;
+  for (const void* p : {x, dg, dfc, w_g, w_fc}) if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
+  const WXPlan p = plan_wx(M, K, N);
+  if (workspace_bytes < p.ws_bytes) return SWG_ERR_WORKSPACE;
+  if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
+  if (!aligned(workspace, 16)) return SWG_ERR_INVALID;
+  {
+    const int64_t w = span_bytes(K, N, es), d = span_bytes(M, N, es);
+    const Span outs[] = {{dx, span_bytes(M, K, es)}, {dw_g, w}, {dw_fc, w},
+                         {workspace, (int64_t)p.ws_bytes}};
+    const Span ins[] = {{x, span_bytes(M, K, es)}, {dg, d}, {dfc, d}, {w_g, w}, {w_fc, w}};
+    if (!outputs_disjoint(outs, ins)) return SWG_ERR_INVALID;
+  }
+  return hip_status(launch_wx(dtype, p, x, dg, dfc, w_g, w_fc, dw_g, dw_fc, dx, M, K, N,
+                              static_cast<float*>(workspace), as_stream(stream)));
+}
+
 // ------------------------------------------------------------------- forward
 swg_status swiglu_fwd(const void* x, const void* w_g, const void* w_fc, const void* b_g,
                       const void* b_fc, void* g, void* fc, void* y, int64_t M, int64_t K,

@@ -530,19 +530,18 @@ __device__ inline void x_odd_groups(std::integer_sequence<int, G...>, f32x16 (&a
 using XGroupsB = std::integer_sequence<int, 0, 1, 2, 3, 4, 5, 6, 7>;
 using XGroupsA = std::integer_sequence<int, 8, 9, 10, 11, 12, 13, 14, 15>;
 
+// The x-stage tile walk of one workgroup: tiles f0, f0 + G, f0 + 2G, ... of the ntiles
+// output tiles, through the LDS ring at `ring` (3 A slots then 2 B slots).
 template <typename T, bool RAGGED>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void x_stage_kernel(
-    const T* __restrict__ dg, const T* __restrict__ dfc, const T* __restrict__ wg,
-    const T* __restrict__ wfc, T* __restrict__ dx, int64_t M, int64_t K, int64_t N, int64_t nq,
-    int64_t ntiles) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[3 * XA_SLOT + 2 * XB_SLOT];
+__device__ __attribute__((always_inline)) inline void x_tiles(
+    uint16_t* ring, const T* __restrict__ dg, const T* __restrict__ dfc,
+    const T* __restrict__ wg, const T* __restrict__ wfc, T* __restrict__ dx, int64_t M,
+    int64_t K, int64_t N, int64_t nq, int64_t ntiles, int64_t f0, int64_t G) {
   uint16_t* const ra0 = ring;
   uint16_t* const rb0 = ring + 3 * XA_SLOT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / WQ, wq = wave % WQ;
-  const int64_t G = gridDim.x;
-  const int64_t f0 = xcd_remap(blockIdx.x, G);
   const int64_t my_tiles = ntiles > f0 ? (ntiles - f0 + G - 1) / G : 0;
   // double stages per dg (or dfc) half, at least 2 so that a tile has at least 4: the A
   // loads run up to three double stages ahead and must stay within the next tile
@@ -655,17 +654,41 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
+constexpr int X_RING_ELEMS = 3 * XA_SLOT + 2 * XB_SLOT;   // 160 KiB
+
+template <typename T, bool RAGGED>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void x_stage_kernel(
+    const T* __restrict__ dg, const T* __restrict__ dfc, const T* __restrict__ wg,
+    const T* __restrict__ wfc, T* __restrict__ dx, int64_t M, int64_t K, int64_t N, int64_t nq,
+    int64_t ntiles) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[X_RING_ELEMS];
+  const int64_t G = gridDim.x;
+  x_tiles<T, RAGGED>(ring, dg, dfc, wg, wfc, dx, M, K, N, nq, ntiles,
+                     xcd_remap(blockIdx.x, G), G);
+}
+
 // ----------------------------------------------------------------- w stage (TN)
 // A = x^T: rows k (K), contraction m;  B = d^T (d = dg or dfc): rows n, contraction m.
-// Work item L = (split s, tile tt): rows [s R, min(M, (s + 1) R)) of the contraction,
-// output rows k0 = (tt / (2 tnh)) * 256, columns n0 of dg (tt % (2 tnh) < tnh) or of dfc.
+// Work item L = (split s, tile tt): output rows k0 = (tt / (2 tnh)) * 256, columns n0 of
+// dg (tt % (2 tnh) < tnh) or of dfc, contracting over the rows of split s.  A split's rows
+// are either one range [s R, min(M, (s + 1) R)) (the w stage) or chunks of CH rows taken
+// every S chunks: chunk j of split s covers rows (s + j S) CH .. (the fused pass, whose
+// x-stage workgroups sweep the same rows at the same time).  Stage st (BR rows) starts at
+//   m_begin + (st >> cs_log2) * stride + (st & (2^cs_log2 - 1)) * BR
+// with cs_log2 = log2(CH / BR) and stride = S CH for chunks, cs_log2 = 30 for one range.
 struct WItem {   // 32-bit fields: M < 2^31 and K, N < 2^22 are checked on the host
-  int s, k0, n0, m_begin, m_end, nst;
+  int s, k0, n0, m_begin, m_end, nst, stride, cs_log2;
   bool hi, live;
 };
 
+struct WMap {          // how items map to rows (see WItem)
+  int64_t split_rows;  // R (one range per split), or 0 for chunked splits
+  int64_t chunk_rows;  // CH (chunked splits; a power of two times BR)
+  int64_t nsplit;      // S
+};
+
 __device__ inline WItem w_item(int64_t L, bool live, int64_t tiles, int64_t tnh,
-                               int64_t split_rows, int64_t M) {
+                               const WMap& mp, int64_t M) {
   WItem w;
   w.live = live;
   const int64_t LL = live ? L : 0;
@@ -675,9 +698,29 @@ __device__ inline WItem w_item(int64_t L, bool live, int64_t tiles, int64_t tnh,
   w.hi = nb >= tnh;
   w.k0 = kb * BP;
   w.n0 = (w.hi ? nb - (int)tnh : nb) * BQ;
-  w.m_begin = w.s * (int)split_rows;
-  w.m_end = (w.m_begin + split_rows < M) ? w.m_begin + (int)split_rows : (int)M;
-  w.nst = 4 * ((w.m_end - w.m_begin + 4 * BR - 1) / (4 * BR));   // whole ring rounds
+  if (mp.split_rows > 0) {
+    w.m_begin = w.s * (int)mp.split_rows;
+    w.m_end = (w.m_begin + mp.split_rows < M) ? w.m_begin + (int)mp.split_rows : (int)M;
+    w.stride = 0;
+    w.cs_log2 = 30;
+    w.nst = 4 * ((w.m_end - w.m_begin + 4 * BR - 1) / (4 * BR));   // whole ring rounds
+  } else {
+    const int ch = (int)mp.chunk_rows;
+    const int chunks = (int)((M + ch - 1) / ch);
+    const int mine = chunks > w.s ? (chunks - w.s + (int)mp.nsplit - 1) / (int)mp.nsplit : 0;
+    w.m_begin = w.s * ch;
+    w.m_end = (int)M;
+    w.stride = (int)mp.nsplit * ch;
+    w.cs_log2 = 31 - __builtin_clz((unsigned)(ch / BR));
+    w.nst = (ch / BR) * mine;                 // a multiple of 4: CH is at least 4 stages
+    // wave-uniform values computed through divisions: pinned to scalar registers, since
+    // they address buffer windows (scalar operands)
+    w.m_begin = __builtin_amdgcn_readfirstlane(w.m_begin);
+    w.stride = __builtin_amdgcn_readfirstlane(w.stride);
+    w.cs_log2 = __builtin_amdgcn_readfirstlane(w.cs_log2);
+    w.nst = __builtin_amdgcn_readfirstlane(w.nst);
+  }
+  if (w.nst < 4) w.nst = 4;                   // one ring round at least (zeros past the end)
   return w;
 }
 
@@ -753,17 +796,17 @@ __device__ inline void w_groups(std::integer_sequence<int, G...>, f32x16 (&acc)[
    ...);
 }
 
+// The w-stage item walk of one workgroup: items f0, f0 + G, ... of the nitems items,
+// through the LDS ring at `ring` (four slots).
 template <typename T, bool RAGGED>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void w_stage_kernel(
-    const T* __restrict__ x, const T* __restrict__ dg, const T* __restrict__ dfc,
-    T* __restrict__ dwg, T* __restrict__ dwfc, float* __restrict__ ws, int64_t M, int64_t K,
-    int64_t N, int64_t tnh, int64_t tiles, int64_t split_rows, int64_t nitems) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[4 * SLOT];
+__device__ __attribute__((always_inline)) inline void w_items(
+    uint16_t* ring, const T* __restrict__ x, const T* __restrict__ dg,
+    const T* __restrict__ dfc, T* __restrict__ dwg, T* __restrict__ dwfc,
+    float* __restrict__ ws, int64_t M, int64_t K, int64_t N, int64_t tnh, int64_t tiles,
+    const WMap& mp, int64_t nitems, int64_t f0, int64_t G) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / WQ, wq = wave % WQ;
-  const int64_t G = gridDim.x;
-  const int64_t f0 = xcd_remap(blockIdx.x, G);
   const int64_t my_items = nitems > f0 ? (nitems - f0 + G - 1) / G : 0;
 
   // A 1 KiB load covers 2 rows x 32 chunks; this wave's loads are rows 8 wave + 2 i +
@@ -780,7 +823,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     dbase[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)lcol[i] * 2u;
   }
   auto issue = [&](const WItem& w, int64_t st, uint16_t* slot) {
-    int m0 = w.m_begin + (int)st * BR;
+    int m0 = w.m_begin + ((int)st >> w.cs_log2) * w.stride +
+             ((int)st & ((1 << w.cs_log2) - 1)) * BR;
     asm volatile("" : "+s"(m0));   // keep per-stage offsets from being hoisted (see x stage)
     const int rows = w.live ? ((w.m_end - m0 < BR) ? w.m_end - m0 : BR) : 0;
     const int64_t mb = rows > 0 ? m0 : 0;
@@ -833,7 +877,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
   f32x16 acc[FP][FQ];
   FragSet<T> frags[2];
-  WItem cur = w_item(f0, my_items > 0, tiles, tnh, split_rows, M);
+  WItem cur = w_item(f0, my_items > 0, tiles, tnh, mp, M);
   // prologue: the first four stages in flight, the first landed for every wave
   w_issue_all<RAGGED>(issue(cur, 0, ring), xbase, dbase, lcol);
   w_issue_all<RAGGED>(issue(cur, 1, ring + SLOT), xbase, dbase, lcol);
@@ -845,7 +889,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   SWG_COMPILER_FENCE();
   const int64_t R2 = 2 * N;
   for (int64_t j = 0; j < my_items; ++j) {
-    const WItem nxt = w_item(f0 + (j + 1) * G, j + 1 < my_items, tiles, tnh, split_rows, M);
+    const WItem nxt = w_item(f0 + (j + 1) * G, j + 1 < my_items, tiles, tnh, mp, M);
     zero_acc(acc);
     W_READ(ring, frags[0]);
     int64_t t = 0;
@@ -884,6 +928,48 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #undef W_STEP
 #undef W_READ
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+}
+
+template <typename T, bool RAGGED>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void w_stage_kernel(
+    const T* __restrict__ x, const T* __restrict__ dg, const T* __restrict__ dfc,
+    T* __restrict__ dwg, T* __restrict__ dwfc, float* __restrict__ ws, int64_t M, int64_t K,
+    int64_t N, int64_t tnh, int64_t tiles, int64_t split_rows, int64_t nitems) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[4 * SLOT];
+  const int64_t G = gridDim.x;
+  const WMap mp{split_rows, 0, 0};
+  w_items<T, RAGGED>(ring, x, dg, dfc, dwg, dwfc, ws, M, K, N, tnh, tiles, mp, nitems,
+                     xcd_remap(blockIdx.x, G), G);
+}
+
+// ------------------------------------------------------------- fused w + x pass
+// One launch for both GEMMs over [dg | dfc] [SwiGLU page, formulas 3 and 4, and the fusion
+// motive of its operator background: no second trip through HBM for an intermediate].
+// Workgroups 0 .. gx - 1 walk the x-stage tiles (row blocks of dx, in order), workgroups
+// gx .. gx + gw - 1 walk w-stage items whose splits take 256-row chunks round-robin, so
+// that in one round both halves of the grid read the same stretch of dg | dfc (at the
+// large-batch shape: 128 x-stage tiles cover 64 row blocks while the 8 splits x 16 dW
+// tiles cover the same 64 chunks); the stretch is read from HBM once and found again in
+// the last-level cache.  The w items' fp32 partials per split are summed by
+// w_reduce_kernel in split order, as in the w stage.
+template <typename T, bool RAGGED>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void wx_fused_kernel(
+    const T* __restrict__ x, const T* __restrict__ dg, const T* __restrict__ dfc,
+    const T* __restrict__ wg, const T* __restrict__ wfc, T* __restrict__ dx,
+    T* __restrict__ dwg, T* __restrict__ dwfc, float* __restrict__ ws, int64_t M, int64_t K,
+    int64_t N, int64_t nq, int64_t x_ntiles, int64_t gx, int64_t tnh, int64_t w_tiles,
+    int64_t chunk_rows, int64_t nsplit, int64_t w_nitems) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[X_RING_ELEMS];
+  static_assert(X_RING_ELEMS >= 4 * SLOT, "the w-stage ring must fit the shared array");
+  const int64_t b = blockIdx.x;
+  if (b < gx) {
+    x_tiles<T, RAGGED>(ring, dg, dfc, wg, wfc, dx, M, K, N, nq, x_ntiles, xcd_remap(b, gx), gx);
+  } else {
+    const int64_t gw = (int64_t)gridDim.x - gx;
+    const WMap mp{0, chunk_rows, nsplit};
+    w_items<T, RAGGED>(ring, x, dg, dfc, dwg, dwfc, ws, M, K, N, tnh, w_tiles, mp, w_nitems,
+                       xcd_remap(b - gx, gw), gw);
+  }
 }
 
 // dw = RNE(dw + sum_s ws[s]) in split order (fp32 dw: no rounding); 4 consecutive columns
@@ -1282,6 +1368,40 @@ hipError_t launch_w_stage(int dtype, const WPlan& p, const void* x, const void* 
   SWG_LAUNCH((w_reduce_kernel<float>), dim3((unsigned)blocks), dim3(256), 0, stream, ws,
                      static_cast<float*>(dw_g), static_cast<float*>(dw_fc), K, N, p.splits);
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t wx_t(const WXPlan& p, const void* x, const void* dg, const void* dfc,
+                       const void* wg, const void* wfc, void* dwg, void* dwfc, void* dx,
+                       int64_t M, int64_t K, int64_t N, float* ws, hipStream_t stream) {
+  float* wsp = p.splits > 1 ? ws : nullptr;
+  const int64_t grid = p.gx + p.gw;
+  // the fast (non-ragged) walks need whole x-stage double stages and whole dW tiles
+  const bool whole = N % XA_BR == 0 && N >= 2 * XA_BR && K % BP == 0 && N % BQ == 0;
+#define SWG_WX_ARGS                                                                          \
+  static_cast<const T*>(x), static_cast<const T*>(dg), static_cast<const T*>(dfc),          \
+      static_cast<const T*>(wg), static_cast<const T*>(wfc), static_cast<T*>(dx),            \
+      static_cast<T*>(dwg), static_cast<T*>(dwfc), wsp, M, K, N, p.nq, p.x_tiles, p.gx,      \
+      p.tn / 2, p.w_tiles, p.chunk_rows, p.splits, p.w_items
+  if (whole)
+    SWG_LAUNCH((wx_fused_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream, SWG_WX_ARGS);
+  else
+    SWG_LAUNCH((wx_fused_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream, SWG_WX_ARGS);
+#undef SWG_WX_ARGS
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  int64_t blocks = ceil_div(K * 2 * N / 4, 256);
+  if (blocks > kMaxStreamBlocks) blocks = kMaxStreamBlocks;
+  SWG_LAUNCH((w_reduce_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, stream, ws,
+             static_cast<T*>(dwg), static_cast<T*>(dwfc), K, N, p.splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_wx(int dtype, const WXPlan& p, const void* x, const void* dg, const void* dfc,
+                     const void* w_g, const void* w_fc, void* dw_g, void* dw_fc, void* dx,
+                     int64_t M, int64_t K, int64_t N, float* ws, hipStream_t stream) {
+  if (dtype == 0) return wx_t<bf16>(p, x, dg, dfc, w_g, w_fc, dw_g, dw_fc, dx, M, K, N, ws, stream);
+  return wx_t<fp16>(p, x, dg, dfc, w_g, w_fc, dw_g, dw_fc, dx, M, K, N, ws, stream);
 }
 
 template <typename T>

@@ -66,6 +66,11 @@ hipError_t launch_w_stage(int dtype, const WPlan& p, const void* x, const void* 
                           const void* dfc, void* dw_g, void* dw_fc, int64_t M, int64_t K,
                           int64_t N, float* ws, int cus, hipStream_t stream);
 
+// fused w + x pass (bf16 / fp16): dx and [dw_g | dw_fc] += x^T [dg | dfc] in one launch
+hipError_t launch_wx(int dtype, const WXPlan& p, const void* x, const void* dg, const void* dfc,
+                     const void* w_g, const void* w_fc, void* dw_g, void* dw_fc, void* dx,
+                     int64_t M, int64_t K, int64_t N, float* ws, hipStream_t stream);
+
 hipError_t launch_x_stage(int dtype, const void* dg, const void* dfc, const void* w_g,
                           const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
                           hipStream_t stream);

@@ -132,4 +132,45 @@ inline WPlan plan_w(int64_t M, int64_t K, int64_t N) {
   return p;
 }
 
+// fused w + x pass: the grid is split between x-stage tiles (gx workgroups) and w-stage
+// items (gw workgroups).  Both GEMMs have the same flop count, so half of the workgroups
+// go to each; the w items are the dW tiles times S splits over 256-row chunks taken
+// round-robin, S chosen so the w half of the grid is filled (and at least 512 rows per
+// split, as in the w stage).  With 128 + 128 workgroups both halves advance through the
+// rows of [dg | dfc] at the same rate.
+struct WXPlan {
+  int64_t nq, x_tiles, gx;         // x stage: column tiles per row block, tiles, workgroups
+  int64_t tn, w_tiles, splits;     // w stage: tile grid, tiles, S
+  int64_t w_items, gw;             // items (tiles x S), workgroups
+  int64_t chunk_rows;              // 256
+  size_t ws_bytes;                 // S > 1: S * K * 2N * sizeof(float)
+};
+
+constexpr int64_t kWXChunkRows = 256;
+constexpr int64_t kWXWorkgroups = 256;
+
+inline WXPlan plan_wx(int64_t M, int64_t K, int64_t N) {
+  WXPlan p{};
+  p.nq = ceil_div(K, kTileQ);
+  p.x_tiles = ceil_div(M, kTileP) * p.nq;
+  p.gx = p.x_tiles < kWXWorkgroups / 2 ? p.x_tiles : kWXWorkgroups / 2;
+  if (p.gx < 1) p.gx = 1;
+  p.tn = 2 * ceil_div(N, kTileQ);
+  p.w_tiles = ceil_div(K, kTileP) * p.tn;
+  const int64_t target = kWXWorkgroups - p.gx;
+  int64_t s = p.w_tiles > 0 ? target / p.w_tiles : 1;
+  const int64_t smax = M / kWMinRowsPerSplit;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  p.splits = s;
+  p.chunk_rows = kWXChunkRows;
+  p.w_items = p.w_tiles * p.splits;
+  p.gw = p.w_items < target ? p.w_items : target;
+  if (p.gw < 1) p.gw = 1;
+  p.ws_bytes = (p.splits > 1 && K > 0 && N > 0)
+                   ? (size_t)p.splits * (size_t)K * (size_t)(2 * N) * sizeof(float)
+                   : 0;
+  return p;
+}
+
 }  // namespace swg

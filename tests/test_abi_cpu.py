@@ -185,6 +185,39 @@ def test_gemm_argument_errors(lib):
     assert lib.swiglu_bwd_x(*xa(dg=ctypes.c_void_p(0x10008))) == UNSUPPORTED
 
 
+def test_fused_wx_argument_errors(lib):
+    import torch
+    M, K, N = 4096, 64, 128
+    need = swg.swiglu_bwd_wx_workspace_size(M, K, N, torch.bfloat16)
+    assert need == swg.swiglu_bwd_wx_workspace_size(M, K, N, torch.float16)
+    assert swg.swiglu_bwd_wx_workspace_size(M, K, N, torch.float32) == 0
+    W_ = ctypes.c_void_p(0x80000)
+    fa = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
+                       (("x", P), ("dg", Q), ("dfc", R), ("wg", S), ("wfc", T), ("dwg", U),
+                        ("dwfc", V), ("dx", W_), ("M", M), ("K", K), ("N", N), ("dt", BF16),
+                        ("w", ctypes.c_void_p(0x100000)), ("wb", need), ("s", NULL))]
+    f = lib.swiglu_bwd_wx
+    assert f(*fa(M=0)) == OK
+    assert f(*fa(K=0, dx=NULL)) == OK
+    assert f(*fa(M=-1)) == INVALID
+    assert f(*fa(dt=9)) == INVALID
+    assert f(*fa(dt=FP32)) == UNSUPPORTED            # 16-bit only
+    assert f(*fa(K=60)) == UNSUPPORTED
+    assert f(*fa(N=100)) == UNSUPPORTED
+    for k in ("x", "dg", "dfc", "wg", "wfc", "dwg", "dwfc", "dx"):
+        assert f(*fa(**{k: NULL})) == NULLPTR, k
+    assert f(*fa(N=0, dx=NULL)) == NULLPTR
+    assert f(*fa(dx=ctypes.c_void_p(0x80008))) == UNSUPPORTED
+    assert f(*fa(dwg=ctypes.c_void_p(0x60004))) == UNSUPPORTED
+    if need > 0:
+        assert f(*fa(wb=need - 1)) == WORKSPACE
+        assert f(*fa(w=NULL)) == NULLPTR
+    # overlaps (a small shape, so the fake buffers are otherwise disjoint)
+    sm = lambda **kw: fa(M=4, K=8, N=8, w=NULL, wb=0, **kw)  # noqa: E731
+    for k, alias in (("dx", P), ("dwg", Q), ("dwfc", U), ("dx", ctypes.c_void_p(0x50040))):
+        assert f(*sm(**{k: alias})) == INVALID, (k, alias)
+
+
 def test_forward_argument_errors(lib):
     M, K, N = 4096, 64, 128
     W_ = ctypes.c_void_p(0x80000)

@@ -112,3 +112,36 @@ def test_full_x_stage(case):
         idx = torch.from_numpy(rows)
         r, a = oracle_x_rows(ref["dg"], ref["dfc"], inp["w_g"], inp["w_fc"], idx)
         compare("dx", dx[idx], r, dt, model_abs=sum_abs_model(a))
+
+
+def test_full_wx_fused(case):
+    """The fused w + x pass in its bench configuration, on the oracle's rounded dg / dfc:
+    dx bit-identical to the x stage's (whose parity is checked above, in full at the
+    large-batch shape) and dW against the oracle (all columns at the large-batch shape,
+    512 sampled columns at the LLM-sized FFN)."""
+    name, dt = case
+    st = _workload(name, dt)
+    dev = device()
+    inp, ref = st["inp"], st["ref"]
+    M, K = inp["x"].shape
+    N = inp["dy"].shape[1]
+    tdt = DTYPES[dt]
+    d = {"x": inp["x"].to(dev), "dg": ref["dg"].to(dev), "dfc": ref["dfc"].to(dev),
+         "w_g": inp["w_g"].to(dev), "w_fc": inp["w_fc"].to(dev)}
+    dw_g = torch.zeros(K, N, dtype=tdt, device=dev)
+    dw_fc = torch.zeros_like(dw_g)
+    dx = torch.empty(M, K, dtype=tdt, device=dev)
+    note(f"fused w+x {name} {dt} M={M} K={K} N={N}")
+    swg.swiglu_bwd_wx(d["x"], d["dg"], d["dfc"], d["w_g"], d["w_fc"], dw_g, dw_fc, dx)
+    dx_sep = torch.empty_like(dx)
+    swg.swiglu_bwd_x(d["dg"], d["dfc"], d["w_g"], d["w_fc"], dx_sep)
+    torch.cuda.synchronize()
+    assert torch.equal(dx.view(torch.int16), dx_sep.view(torch.int16)), "dx"
+    del dx, dx_sep, d
+    cols = None
+    if N > 4096:
+        cols = np.sort(np.random.default_rng(23).choice(N, 512, replace=False))
+    rg, rf, ag, af = oracle_w_chunked(inp["x"], ref["dg"], ref["dfc"], cols=cols)
+    sel = slice(None) if cols is None else torch.from_numpy(cols)
+    compare("fused dw_g", dw_g.cpu()[:, sel], rg, dt, model_abs=sum_abs_model(ag))
+    compare("fused dw_fc", dw_fc.cpu()[:, sel], rf, dt, model_abs=sum_abs_model(af))
