@@ -313,6 +313,47 @@ __device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane_in, F
       }
 }
 
+// dW[row, col] += accumulators of block row I (32 rows of the wave's 128), for a tile
+// without an M split.  `r` is a buffer window over the wave's valid dW rows (rows past K
+// are dropped by the range check); columns past N are pushed out of the window
+// (cols_left: columns left from the wave's first).  The old values of all of the block's
+// pairs are loaded before any of them is stored: the compiler cannot move a load of dW
+// above a store to dW, so a load-add-store per pair would cost one memory round trip each
+// (128 per wave); batched, the wave makes four.  Offsets are 32-bit (128 rows of < 2^23
+// bytes).
+template <typename T, int I>
+__device__ inline void rmw_block_rows(const f32x16 (&acc)[FP][FQ], int lane,
+                                      __amdgpu_buffer_rsrc_t r, uint32_t row_bytes,
+                                      int cols_left) {
+  const int odd = lane & 1;
+  const uint32_t loff = (uint32_t)(4 * (lane >> 5) + odd) * row_bytes +
+                        (uint32_t)((lane & 31) & ~1) * 2u;
+  uint32_t voff[FQ][8], old[FQ][8];
+#pragma unroll
+  for (int j = 0; j < FQ; ++j) {
+    const uint32_t cbad = j * 32 + ((lane & 31) & ~1) < cols_left ? 0u : kOOB;
+#pragma unroll
+    for (int r2 = 0; r2 < 8; ++r2) {
+      const int rr = 2 * r2;
+      voff[j][r2] = (loff + (uint32_t)(I * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes +
+                     64u * j) | cbad;
+      old[j][r2] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff[j][r2], 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < FQ; ++j)
+#pragma unroll
+    for (int r2 = 0; r2 < 8; ++r2) {
+      const int rr = 2 * r2;
+      const float v0 = acc[I][j][rr], v1 = acc[I][j][rr + 1];
+      const float recv = swap_adjacent(odd ? v0 : v1);
+      const float lo = odd ? recv : v0, hi = odd ? v1 : recv;
+      const float2 o = unpack2<T>(old[j][r2]);
+      __builtin_amdgcn_raw_buffer_store_b32(pack2<T>(o.x + lo, o.y + hi), r, (int)voff[j][r2],
+                                            0, 0);
+    }
+}
+
 // Tile store straight from the accumulators: every lane pair turns its two rows x two
 // columns into one row each (pack to 16 bits, swap the packed words with the neighbouring
 // lane, byte-permute: even lanes keep row R, odd lanes row R + 1) and writes 32 bits per
@@ -914,14 +955,16 @@ __device__ __attribute__((always_inline)) inline void w_items(
       });
     } else {
       T* dw = cur.hi ? dwfc : dwg;
-      for_each_pair(acc, lane, [&](int row, int col, float lo, float hi) {
-        const int64_t k = k0 + row, n = n0 + col;
-        if (k < K && n < N) {
-          uint32_t* p = reinterpret_cast<uint32_t*>(dw + k * N + n);
-          const float2 old = unpack2<T>(*p);
-          *p = pack2<T>(old.x + lo, old.y + hi);
-        }
-      });
+      int ln = lane;
+      asm volatile("" : "+v"(ln));   // lane terms formed here, not hoisted (see for_each_pair)
+      const int64_t krows = K - k0 < 128 ? K - k0 : 128;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(dw + k0 * N + n0, clamp_bytes(krows, N * 2));
+      const uint32_t row_bytes = (uint32_t)(N * 2);
+      const int cols_left = (int)(N - n0);
+      rmw_block_rows<T, 0>(acc, ln, r, row_bytes, cols_left);
+      rmw_block_rows<T, 1>(acc, ln, r, row_bytes, cols_left);
+      rmw_block_rows<T, 2>(acc, ln, r, row_bytes, cols_left);
+      rmw_block_rows<T, 3>(acc, ln, r, row_bytes, cols_left);
     }
     cur = nxt;
   }

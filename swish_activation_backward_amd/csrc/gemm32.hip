@@ -202,10 +202,20 @@ __global__ __launch_bounds__(NT32) void w_stage32_kernel(const float* __restrict
       if (k < K && n < N) dst[k * 2 * N + n] = v;
     });
   } else {
+    // dw += C: every old value is loaded before any store (a load-add-store per element
+    // would be one memory round trip each, since loads of dw cannot move above its stores)
     float* dw = hi ? dwfc : dwg;
+    float old[64];
+    int e = 0;
+    for_each_acc32(acc, wp, wq, lane, [&](int row, int col, float) {
+      const int64_t k = k0 + row, n = n0 + col;
+      old[e++] = (k < K && n < N) ? dw[k * N + n] : 0.0f;
+    });
+    e = 0;
     for_each_acc32(acc, wp, wq, lane, [&](int row, int col, float v) {
       const int64_t k = k0 + row, n = n0 + col;
-      if (k < K && n < N) dw[k * N + n] += v;
+      if (k < K && n < N) dw[k * N + n] = old[e] + v;
+      ++e;
     });
   }
 }
