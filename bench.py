@@ -328,22 +328,52 @@ def cpu_baseline(inp, sw_inputs, rows, swish_len):
     wg, wf = f64(inp["w_g"]), f64(inp["w_fc"])
     swish_len = min(swish_len, sw_inputs["fp32"]["grad"].numel())
     sw = {dt: (f64(v["grad"][:swish_len]), f64(v["x"][:swish_len])) for dt, v in sw_inputs.items()}
+    stages = {}
+
+    def timed(name, fn):
+        """Run one oracle stage; record its wall seconds and the cores it kept busy
+        (process CPU time over wall time, all threads of the process)."""
+        w0, c0 = time.perf_counter(), time.process_time()
+        out = fn()
+        w, c = time.perf_counter() - w0, time.process_time() - c0
+        stages[name] = {"seconds": round(w, 4), "cores_used": round(c / w, 2) if w > 0 else None}
+        return out
+
+    # the element-wise stages run before the matmuls: BLAS worker threads spin for a while
+    # after a matmul, which would be counted against the stage that follows it
     t0 = time.perf_counter()
-    dg, dfc, _, _ = R.b_ref(dy, g, fc)
-    R.w_ref(x, dg, dfc)
-    R.x_ref(dg, dfc, wg, wf)
+    dg, dfc, _, _ = timed("b", lambda: R.b_ref(dy, g, fc))
     for dt in SWISH_DTYPES:
-        R.swish_grad_ref(sw[dt][0], sw[dt][1], SWISH_BETA)
+        timed(f"swish_grad_{dt}", lambda dt=dt: R.swish_grad_ref(sw[dt][0], sw[dt][1], SWISH_BETA))
+    timed("w", lambda: R.w_ref(x, dg, dfc))
+    timed("x", lambda: R.x_ref(dg, dfc, wg, wf))
     t = time.perf_counter() - t0
     work = stage_work(m, K, N, swish_len)
     t_roof = sum(v["t_roof"] for v in work.values())
+    used = max(v["cores_used"] or 0 for v in stages.values())
     return {"value": round(100.0 * t_roof / t, 6), "unit": "% of roofline",
-            "cores": int(blas_threads), "kind": "oracle",
-            "seconds": round(t, 3),
+            "cores": max(1, int(round(used))), "kind": "oracle",
+            "seconds": round(t, 3), "stages": stages,
+            "blas": _blas_info(), "host_cores": len(os.sched_getaffinity(0)),
+            "blas_threads": int(blas_threads),
             "sample": f"{m} of {M} rows (b, w, x stages) and {swish_len} elements of the "
-                      f"Swish input per dtype (whole workload when equal); numpy float64, "
-                      f"element-wise work on 1 thread, GEMMs on {blas_threads} BLAS threads",
+                      f"Swish input per dtype (whole workload when equal); numpy float64; "
+                      f"cores = the most any stage kept busy (stages.*.cores_used: process "
+                      f"CPU time / wall time; numpy element-wise stages run on one thread, "
+                      f"the w and x matmuls on the BLAS threads)",
             "cpu": _cpu_model()}
+
+
+def _blas_info():
+    """The BLAS library numpy calls (threadpoolctl), e.g. 'openblas 0.3.x'."""
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def _cpu_model():
