@@ -214,7 +214,8 @@ def time_swish_context(swg, steps):
 
 
 def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
-    """The b, w and x stages at the other SwiGLU workloads (same seeded recipe), each
+    """The b, w and x stages and the fused w + x pass at the other SwiGLU workloads (same
+    seeded recipe), each
     stage call preceded by a 1 GiB write that evicts the 256 MB last-level cache (the
     tiny and ragged working sets would otherwise stay in it) and timed by its kernel span,
     median over `steps` calls.  Reported beside the step (the tiny and ragged
@@ -240,11 +241,15 @@ def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
                            dtype=torch.uint8, device=dev)
         ws_w = torch.empty(max(1, swg.swiglu_bwd_w_workspace_size(M, K, N, torch.bfloat16)),
                            dtype=torch.uint8, device=dev)
+        ws_wx = torch.empty(max(1, swg.swiglu_bwd_wx_workspace_size(M, K, N, torch.bfloat16)),
+                            dtype=torch.uint8, device=dev)
         calls = {
             "b": lambda: swg.swiglu_bwd_b(d["dy"], d["g"], d["fc"], dg, dfc, db_g, db_fc,
                                           workspace=ws_b),
             "w": lambda: swg.swiglu_bwd_w(d["x"], dg, dfc, dw_g, dw_fc, workspace=ws_w),
             "x": lambda: swg.swiglu_bwd_x(dg, dfc, d["w_g"], d["w_fc"], dx),
+            "fused_wx": lambda: swg.swiglu_bwd_wx(d["x"], dg, dfc, d["w_g"], d["w_fc"], dw_g,
+                                                  dw_fc, dx, workspace=ws_wx),
         }
         for _ in range(warmup):
             for f in calls.values():
@@ -257,6 +262,9 @@ def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
                 f()
         torch.cuda.synchronize()
         work = stage_work(M, K, N, 0)
+        work["fused_wx"] = {"flops": work["w"]["flops"] + work["x"]["flops"],
+                            "t_roof": work["w"]["t_roof"] + work["x"]["t_roof"],
+                            "bound": work["w"]["bound"]}
         out = {"M": M, "K": K, "N": N}
         for i, st in enumerate(calls):
             ts = sorted(timer.seconds(it * len(calls) + i) for it in range(steps))
@@ -270,7 +278,7 @@ def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
                 e["GB/s"] = round(wk["bytes"] / t / 1e9, 1)
             out[st] = e
         res[name] = out
-        del calls, d, dg, dfc, dx, dw_g, dw_fc, ws_b, ws_w
+        del calls, d, dg, dfc, dx, dw_g, dw_fc, ws_b, ws_w, ws_wx
         torch.cuda.empty_cache()
     return res
 
