@@ -1,6 +1,7 @@
 """The backward path captured in a HIP graph (torch.cuda.CUDAGraph on ROCm): every library
-call is capturable (no allocation, no memset nodes; accumulators are cleared with torch's
-fill kernel inside the graph).  The graph is replayed several times with eager work and
+call, the static-scratch b stage and the fused w + x pass included, is capturable (no
+allocation, no memset nodes; accumulators are cleared with torch's fill kernel inside the
+graph).  The graph is replayed several times with eager work and
 synchronisations in between, and every replay is compared bit for bit with the eager run."""
 from __future__ import annotations
 
@@ -31,16 +32,29 @@ def test_backward_graph_replays_match_eager():
                        device=dev)
     ws_w = torch.empty(max(1, swg.swiglu_bwd_w_workspace_size(M, K, N, bf)), dtype=torch.uint8,
                        device=dev)
-    outs = (dg, dfc, db_g, db_fc, dw_g, dw_fc, dx, gs, fs, ys, gx)
+    # the static-scratch b stage and the fused w + x pass into outputs of their own
+    dg2, dfc2 = torch.empty_like(dg), torch.empty_like(dfc)
+    db_g2, db_fc2 = torch.empty_like(db_g), torch.empty_like(db_fc)
+    dw_g3, dw_fc3, dx3 = torch.empty_like(dw_g), torch.empty_like(dw_fc), torch.empty_like(dx)
+    ws_wx = torch.empty(max(1, swg.swiglu_bwd_wx_workspace_size(M, K, N, bf)),
+                        dtype=torch.uint8, device=dev)
+    outs = (dg, dfc, db_g, db_fc, dw_g, dw_fc, dx, gs, fs, ys, gx, dg2, dfc2, db_g2, db_fc2,
+            dw_g3, dw_fc3, dx3)
+    names = ("dg", "dfc", "db_g", "db_fc", "dw_g", "dw_fc", "dx", "g", "fc", "y", "swish",
+             "noalloc dg", "noalloc dfc", "noalloc db_g", "noalloc db_fc", "fused dw_g",
+             "fused dw_fc", "fused dx")
 
     def step():
-        for t in (db_g, db_fc, dw_g, dw_fc):
+        for t in (db_g, db_fc, dw_g, dw_fc, db_g2, db_fc2, dw_g3, dw_fc3):
             t.zero_()
         swg.swiglu_bwd_b(d["dy"], d["g"], d["fc"], dg, dfc, db_g, db_fc, workspace=ws_b)
         swg.swiglu_bwd_w(d["x"], dg, dfc, dw_g, dw_fc, workspace=ws_w)
         swg.swiglu_bwd_x(dg, dfc, d["w_g"], d["w_fc"], dx)
         swg.swiglu_fwd(d["x"], d["w_g"], d["w_fc"], d["b_g"], d["b_fc"], gs, fs, ys)
         swg.swish_grad(d["dy"], d["g"], grad_x=gx, beta=1.702)
+        swg.swiglu_bwd_b_noalloc(d["dy"], d["g"], d["fc"], dg2, dfc2, db_g2, db_fc2)
+        swg.swiglu_bwd_wx(d["x"], dg, dfc, d["w_g"], d["w_fc"], dw_g3, dw_fc3, dx3,
+                          workspace=ws_wx)
 
     note("graph: eager reference")
     step()
@@ -65,6 +79,8 @@ def test_backward_graph_replays_match_eager():
         note(f"graph: replay {rep}")
         graph.replay()
         torch.cuda.synchronize()
-        for name, t, w in zip(("dg", "dfc", "db_g", "db_fc", "dw_g", "dw_fc", "dx", "g", "fc",
-                               "y", "swish"), outs, want):
+        for name, t, w in zip(names, outs, want):
             assert torch.equal(t.view(torch.int16), w), f"replay {rep}: {name} differs"
+    # the static-scratch b stage gives the workspace entry point's bits
+    for a, b in ((dg2, dg), (dfc2, dfc), (db_g2, db_g), (db_fc2, db_fc), (dx3, dx)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
