@@ -134,6 +134,27 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
                         void* stream);
 
 /*
+ * Tile configuration of the matrix-core stages: the edge of the square output tile (rows
+ * = columns per workgroup) that swiglu_bwd_w (stage 0), swiglu_bwd_x (stage 1) or
+ * swiglu_bwd_wx (stage 2) uses for a bf16 or fp16 problem of this shape: 256, or 128 where
+ * 256 x 256 tiles would leave CUs of the MI355X idle (small M, small outputs) or, in the w
+ * stage, need many fp32 M-split partials.  Host-only arithmetic: the planner the calls
+ * themselves use, independent of the device.  Results do not depend on the tile size
+ * beyond rounding order.  0 for fp32 (its own kernels), empty or unsupported shapes and an
+ * unknown stage.
+ */
+int swiglu_bwd_gemm_tile(int stage, int64_t M, int64_t K, int64_t N, swg_dtype dtype);
+
+/*
+ * Tile override, for tuning and tests: edge 256 or 128 makes swiglu_bwd_w, swiglu_bwd_x,
+ * swiglu_bwd_wx, their workspace-size queries and swiglu_bwd_gemm_tile, when called
+ * afterwards on the calling thread, use that tile edge instead of the planner's choice
+ * (bf16 / fp16; the w stage's M splits follow the tile count, so query the workspace size
+ * under the same setting); 0 restores the planner.  SWG_ERR_INVALID for other values.
+ */
+swg_status swg_set_gemm_tile(int edge);
+
+/*
  * Fused w + x pass [SwiGLU page, formulas 3 and 4, which contract the same [dg | dfc], and
  * the operator background's motive for fusion: intermediates should not make repeated
  * trips through memory]: the results of swiglu_bwd_w followed by swiglu_bwd_x from one

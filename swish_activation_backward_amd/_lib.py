@@ -17,7 +17,7 @@ __all__ = ["SwgError", "load_library", "library_path", "swish_grad", "swish_grad
            "swiglu_bwd_b", "swiglu_bwd_b_noalloc", "swiglu_bwd_w", "swiglu_bwd_x", "swiglu_fwd",
            "swiglu_bwd_b_workspace_size", "swiglu_bwd_w_workspace_size", "swg_version",
            "swg_time_next_call", "swiglu_bwd_wx", "swiglu_bwd_wx_workspace_size",
-           "DTYPE_CODE", "STATUS"]
+           "swiglu_bwd_gemm_tile", "swg_set_gemm_tile", "DTYPE_CODE", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libswiglu_bwd.so"
@@ -79,6 +79,10 @@ def load_library():
         lib.swiglu_bwd_wx.restype = i32
         lib.swiglu_bwd_wx_workspace_size.argtypes = [i64, i64, i64, i32]
         lib.swiglu_bwd_wx_workspace_size.restype = sz
+        lib.swiglu_bwd_gemm_tile.argtypes = [i32, i64, i64, i64, i32]
+        lib.swiglu_bwd_gemm_tile.restype = i32
+        lib.swg_set_gemm_tile.argtypes = [i32]
+        lib.swg_set_gemm_tile.restype = i32
         lib.swiglu_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
         lib.swiglu_fwd.restype = i32
         lib.swg_status_string.argtypes = [i32]
@@ -331,6 +335,23 @@ def swiglu_bwd_x(dg, dfc, w_g, w_fc, dx, stream=None):
 
 def swiglu_bwd_wx_workspace_size(M: int, K: int, N: int, dtype) -> int:
     return int(load_library().swiglu_bwd_wx_workspace_size(M, K, N, DTYPE_CODE[dtype]))
+
+
+_GEMM_STAGE = {"w": 0, "x": 1, "wx": 2}
+
+
+def swiglu_bwd_gemm_tile(stage: str, M: int, K: int, N: int, dtype) -> int:
+    """Output tile edge (256 or 128) the planner picks for stage "w", "x" or "wx" (the fused
+    pass) at this shape; 0 where the stage does not use the bf16 / fp16 tiles."""
+    return int(load_library().swiglu_bwd_gemm_tile(_GEMM_STAGE[stage], M, K, N,
+                                                   DTYPE_CODE[dtype]))
+
+
+def swg_set_gemm_tile(edge: int) -> None:
+    """Make the GEMM calls (and workspace queries) on this thread use tile edge 256 or 128
+    instead of the planner's choice; 0 restores the planner."""
+    lib = load_library()
+    _check("swg_set_gemm_tile", lib.swg_set_gemm_tile(int(edge)), lib)
 
 
 def swiglu_bwd_wx(x, dg, dfc, w_g, w_fc, dw_g, dw_fc, dx, workspace=None, stream=None):

@@ -103,7 +103,18 @@ int gemm_grid_cap() {
 
 swg::CallTiming& swg::call_timing() { return g_timing; }
 
+namespace {
+// swg_set_gemm_tile's setting for this thread: 4 or 2 (tile edge / 64), 0 = planner
+thread_local int g_tile_f = 0;
+}  // namespace
+
 extern "C" {
+
+swg_status swg_set_gemm_tile(int edge) {
+  if (edge != 0 && edge != 128 && edge != 256) return SWG_ERR_INVALID;
+  g_tile_f = edge / 64;
+  return SWG_OK;
+}
 
 swg_status swg_time_next_call(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr)) return SWG_ERR_INVALID;
@@ -351,7 +362,7 @@ static swg_status gemm_shape_check(int dtype, int64_t M, int64_t K, int64_t N,
 
 size_t swiglu_bwd_w_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dtype) {
   if (gemm_shape_check(dtype, M, K, N, true) != SWG_OK || M == 0 || K == 0 || N == 0) return 0;
-  return plan_w(M, K, N).ws_bytes;
+  return plan_w(M, K, N, g_tile_f).ws_bytes;
 }
 
 swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc, void* dw_g, void* dw_fc,
@@ -364,7 +375,7 @@ swg_status swiglu_bwd_w(const void* x, const void* dg, const void* dfc, void* dw
   if (!x || !dg || !dfc || !dw_g || !dw_fc) return SWG_ERR_NULLPTR;
   for (const void* p : {x, dg, dfc}) if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
   for (const void* p : {(const void*)dw_g, (const void*)dw_fc}) if (!aligned(p, 8)) return SWG_ERR_UNSUPPORTED;
-  const WPlan p = plan_w(M, K, N);
+  const WPlan p = plan_w(M, K, N, g_tile_f);
   if (workspace_bytes < p.ws_bytes) return SWG_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
   if (!aligned(workspace, 16)) return SWG_ERR_INVALID;
@@ -400,8 +411,19 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
     const Span ins[] = {{dg, d}, {dfc, d}, {w_g, w}, {w_fc, w}};
     if (!outputs_disjoint(outs, ins)) return SWG_ERR_INVALID;
   }
-  return hip_status(launch_x_stage(dtype, dg, dfc, w_g, w_fc, dx, M, K, N, gemm_grid_cap(),
-                                   as_stream(stream)));
+  return hip_status(launch_x_stage(dtype, dg, dfc, w_g, w_fc, dx, M, K, N, g_tile_f,
+                                   gemm_grid_cap(), as_stream(stream)));
+}
+
+int swiglu_bwd_gemm_tile(int stage, int64_t M, int64_t K, int64_t N, swg_dtype dtype) {
+  if (dtype == SWG_FP32 || gemm_shape_check(dtype, M, K, N) != SWG_OK || M == 0 || K == 0 ||
+      N == 0)
+    return 0;
+  int f = 0;
+  if (stage == 0) f = plan_w(M, K, N, g_tile_f).f;
+  else if (stage == 1) f = plan_x(M, K, N, g_tile_f).f;
+  else if (stage == 2) f = plan_wx(M, K, N, g_tile_f).f;
+  return (int)tile_edge(f);
 }
 
 // ------------------------------------------------------------------- fused w + x
@@ -409,7 +431,7 @@ size_t swiglu_bwd_wx_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype d
   if (dtype == SWG_FP32 || gemm_shape_check(dtype, M, K, N) != SWG_OK || M == 0 || K == 0 ||
       N == 0)
     return 0;
-  return plan_wx(M, K, N).ws_bytes;
+  return plan_wx(M, K, N, g_tile_f).ws_bytes;
 }
 
 swg_status swiglu_bwd_wx(const void* x, const void* dg, const void* dfc, const void* w_g,
@@ -429,7 +451,7 @@ swg_status swiglu_bwd_wx(const void* x, const void* dg, const void* dfc, const v
   for (const void* p : {(const void*)dw_g, (const void*)dw_fc})
     if (!aligned(p, 8)) return SWG_ERR_UNSUPPORTED;
   for (const void* p : {x, dg, dfc, w_g, w_fc}) if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
-  const WXPlan p = plan_wx(M, K, N);
+  const WXPlan p = plan_wx(M, K, N, g_tile_f);
   if (workspace_bytes < p.ws_bytes) return SWG_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
   if (!aligned(workspace, 16)) return SWG_ERR_INVALID;

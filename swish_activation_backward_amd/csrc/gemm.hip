@@ -75,6 +75,25 @@ constexpr int SLOT = (BP + BQ) * BR;                    // elements per ring slo
 constexpr int LOADS_PER_STAGE = SLOT * 2 / 1024 / (NT / 64);   // 1 KiB loads per wave: 8
 constexpr uint32_t kOOB = 0x80000000u;  // offset past every window: loads zeros
 static_assert(BR == 32 && BP == 256 && BQ == 256, "swizzles below assume 256 x 256 x 32");
+constexpr int XA_BR = 2 * BR;   // x stage: contraction elements per double stage
+
+// Workgroup tile configurations of the w and x stages.  F = 4: 256 x 256 outputs, each
+// wave 128 x 128 (4 x 4 MFMA tiles, 256 accumulators); F = 2: 128 x 128 outputs, each wave
+// 64 x 64 (2 x 2 tiles), for outputs whose 256 x 256 tiles would leave most CUs idle.  The
+// loops, swizzles and ring layouts are the same; only the tile edge changes.
+template <int F> struct Tc {
+  static_assert(F == 2 || F == 4, "tile configurations");
+  static constexpr int P = 64 * F;                       // tile edge (rows = columns)
+  static constexpr int WR = 32 * F;                      // rows / columns per wave
+  static constexpr int XSLOT = P * XA_BR;                // x stage: elements per A or B slot
+  static constexpr int XLOADS = XSLOT * 2 / 1024 / (NT / 64);   // 1 KiB loads per wave: 2F
+  static constexpr int X_RING = 5 * XSLOT;               // 3 A slots + 2 B slots
+  static constexpr int WSLOT = 2 * P * BR;               // w stage: elements per ring slot
+  static constexpr int WLOADS = WSLOT * 2 / 1024 / (NT / 64);   // 1 KiB loads per wave: 2F
+  static constexpr int W_RING = 4 * WSLOT;
+  static constexpr int RPL = 1024 / (2 * P);             // w-stage rows per 1 KiB load
+  static constexpr int RING = X_RING > W_RING ? X_RING : W_RING;
+};
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
 constexpr int vmcnt_le(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14); }
@@ -117,11 +136,12 @@ __device__ inline int64_t xcd_remap(int64_t b, int64_t nblocks) {
   return (b % 8) * per + b / 8;
 }
 
-__device__ inline void zero_acc(f32x16 (&acc)[FP][FQ]) {
+template <int F>
+__device__ inline void zero_acc(f32x16 (&acc)[F][F]) {
 #pragma unroll
-  for (int i = 0; i < FP; ++i)
+  for (int i = 0; i < F; ++i)
 #pragma unroll
-    for (int j = 0; j < FQ; ++j)
+    for (int j = 0; j < F; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
@@ -139,15 +159,15 @@ __device__ inline void zero_acc(f32x16 (&acc)[FP][FQ]) {
 __device__ inline int xsw(int r) { return (r >> 2) & 3; }
 
 // Scheduling hint for one pipeline step: the LDS reads of the next stage (READS of them)
-// spread evenly between the 32 MFMAs of the current stage.  sched_group_barrier(mask, n,
+// spread evenly between the MFMAS MFMAs of the current stage.  sched_group_barrier(mask, n,
 // 0) asks the scheduler for n instructions of the class next (0x008 MFMA, 0x100 LDS read).
 #define SWG_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-template <int READS>
+template <int MFMAS, int READS>
 __device__ inline void step_schedule() {
-  static_assert(READS == 16 || READS == 24 || READS == 32, "reads per step");
-  // groups of (MFMAs, reads) that cover 32 MFMAs and READS reads evenly
-  constexpr int kGroups = READS == 24 ? 8 : READS;
-  constexpr int kMfma = 32 / kGroups, kReads = READS / kGroups;
+  static_assert((MFMAS == 32 && READS == 16) || (MFMAS == 8 && READS == 8), "per step");
+  // groups of (MFMAs, reads) that cover the step's MFMAs and reads evenly
+  constexpr int kGroups = READS;
+  constexpr int kMfma = MFMAS / kGroups, kReads = READS / kGroups;
 #pragma unroll
   for (int q = 0; q < kGroups; ++q) {
     SWG_SCHED(0x008, kMfma);
@@ -157,49 +177,44 @@ __device__ inline void step_schedule() {
 
 // Operand fragments of one stage, per wave: [contraction half][block]; FragSet[2] holds
 // the stage being multiplied and the stage being read.
-template <typename T> struct FragSet {
-  typename Mfma<T>::frag a[2][FP], b[2][FQ];
+template <typename T, int F = 4> struct FragSet {
+  typename Mfma<T>::frag a[2][F], b[2][F];
 };
 
 // x-stage LDS: both operands move 64 contraction elements (128-byte row segments) per
 // load, into "double stages" (pipeline stage 2d + h is half h of double stage d).  A ring
-// (dg | dfc, streamed from HBM): three slots of [256 rows][64]; B ring (W, resident in L2):
-// two slots of [256 rows][64]; 160 KiB in all.  A row is 8 chunks of 16 B, chunk c of row r
-// at position c ^ xsw8(r): within 16 consecutive rows the pairs of rows that share a
-// 256-byte bank window take different chunks.
-constexpr int XA_BR = 2 * BR;                 // contraction elements per double stage
-constexpr int XA_SLOT = BP * XA_BR;           // elements per A slot (32 KiB)
-constexpr int XB_SLOT = BQ * XA_BR;           // elements per B slot (32 KiB)
-constexpr int XA_LOADS = XA_SLOT * 2 / 1024 / (NT / 64);   // 1 KiB loads per wave: 8
-constexpr int XB_LOADS = XB_SLOT * 2 / 1024 / (NT / 64);   // 8
+// (dg | dfc, streamed from HBM): three slots of [P rows][64]; B ring (W, resident in L2):
+// two slots of [P rows][64]; 160 KiB in all at P = 256.  A row is 8 chunks of 16 B, chunk
+// c of row r at position c ^ xsw8(r): within 16 consecutive rows the pairs of rows that
+// share a 256-byte bank window take different chunks.
 __device__ inline int xsw8(int r) { return (r >> 1) & 7; }
 
 // Fragments of one pipeline stage: half HALF of an A slot and of a B slot.
-template <typename T, int HALF>
+template <typename T, int F, int HALF>
 __device__ inline void x_read(const uint16_t* aslot, const uint16_t* bslot, int wp, int wq,
-                              int lane, FragSet<T>& f) {
-  using F = typename Mfma<T>::frag;
+                              int lane, FragSet<T, F>& f) {
+  using Fr = typename Mfma<T>::frag;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int lc = 2 * kk + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < FP; ++i) {
-      const int r = wp * 128 + i * 32 + (lane & 31);
-      f.a[kk][i] = *reinterpret_cast<const F*>(aslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
+    for (int i = 0; i < F; ++i) {
+      const int r = wp * Tc<F>::WR + i * 32 + (lane & 31);
+      f.a[kk][i] = *reinterpret_cast<const Fr*>(aslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
     }
 #pragma unroll
-    for (int j = 0; j < FQ; ++j) {
-      const int r = wq * 128 + j * 32 + (lane & 31);
-      f.b[kk][j] = *reinterpret_cast<const F*>(bslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
+    for (int j = 0; j < F; ++j) {
+      const int r = wq * Tc<F>::WR + j * 32 + (lane & 31);
+      f.b[kk][j] = *reinterpret_cast<const Fr*>(bslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
     }
   }
 }
 
 // ------------------------------------------------------------------ w-stage tiles
-// Slot layout: [32 contraction rows of A][256] then [32 rows of B][256]; a row is 32
-// chunks of 16 B, chunk c of row m at position c ^ wsw(m).  A transposing read covers
-// 4 rows x 32 bytes per 16 lanes (64 bytes for 32 lanes); wsw spreads them over
-// distinct banks.
+// Slot layout: [32 contraction rows of A][P] then [32 rows of B][P]; a row is P / 8
+// chunks of 16 B (32 or 16), chunk c of row m at position c ^ wsw(m).  A transposing read
+// covers 4 rows x 32 bytes per 16 lanes (64 bytes for 32 lanes); wsw spreads them over
+// distinct banks (rows are a multiple of 256 bytes apart at either P).
 __device__ inline int wsw(int m) {
   const int t = m & 3;
   return t == 0 ? 0 : t == 1 ? 6 : t == 2 ? 12 : 10;
@@ -214,50 +229,54 @@ __device__ inline i16x4 tr_read(const uint16_t* p) {
 }
 
 // Per-lane part of the transposing-read address of operand block i (rows 32 i .. of the
-// wave's 128), in elements, for contraction rows 0..3 of a 16-row step:
+// wave's WR), in elements, for contraction rows 0..3 of a 16-row step, in a [k][P] tile
+// whose wave part starts at chunk wchunk:
 //   lane = 16 grp + s:  row 8 (grp / 2) + s / 4, column 32 i + 16 (grp % 2) + 4 (s % 4)
 // with the column's chunk swizzled by wsw(row) (row % 4 = s / 4: the swizzle does not
-// depend on the step or on i's contribution above bit 3, so every other term is a
-// compile-time offset).
-__device__ inline void w_lane_offsets(int lane, int (&off)[FP]) {
+// depend on the step, so every other term is a compile-time offset).
+template <int F, int P>
+__device__ inline void w_lane_offsets(int lane, int wchunk, int (&off)[F]) {
   const int grp = lane >> 4, s = lane & 15;
   const int q = 2 * (grp & 1) + ((s & 3) >> 1);    // chunk inside the 32-column block
   const int sw = wsw(s >> 2);
   const int row = 8 * (grp >> 1) + (s >> 2);
 #pragma unroll
-  for (int i = 0; i < FP; ++i) off[i] = row * BQ + (((4 * i + q) ^ sw) << 3) + 4 * (s & 1);
+  for (int i = 0; i < F; ++i)
+    off[i] = row * P + (((wchunk + 4 * i + q) ^ sw) << 3) + 4 * (s & 1);
 }
 
-template <typename T>
-__device__ inline typename Mfma<T>::frag w_frag(const uint16_t* p) {
-  // p: this lane's address for contraction rows 0..3; rows 4..7 are 4 rows further
+// Transposing-read fragment of 16 contraction rows from a [k][RL] tile: p is this lane's
+// address for contraction rows 0..3; rows 4..7 are 4 rows further.
+template <typename T, int RL>
+__device__ inline typename Mfma<T>::frag tr_frag(const uint16_t* p) {
   const i16x4 lo = tr_read(p);
-  const i16x4 hi = tr_read(p + 4 * BQ);
+  const i16x4 hi = tr_read(p + 4 * RL);
   const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(typename Mfma<T>::frag, v);
 }
 
-template <typename T>
-__device__ inline void w_read(const uint16_t* slot, const int (&aoff)[FP], const int (&boff)[FQ],
-                              FragSet<T>& f) {
+template <typename T, int F>
+__device__ inline void w_read(const uint16_t* slot, const int (&aoff)[F], const int (&boff)[F],
+                              FragSet<T, F>& f) {
+  constexpr int P = Tc<F>::P;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int i = 0; i < FP; ++i) f.a[ks][i] = w_frag<T>(slot + 16 * ks * BQ + aoff[i]);
+    for (int i = 0; i < F; ++i) f.a[ks][i] = tr_frag<T, P>(slot + 16 * ks * P + aoff[i]);
 #pragma unroll
-    for (int j = 0; j < FQ; ++j) f.b[ks][j] = w_frag<T>(slot + BR * BP + 16 * ks * BQ + boff[j]);
+    for (int j = 0; j < F; ++j) f.b[ks][j] = tr_frag<T, P>(slot + BR * P + 16 * ks * P + boff[j]);
   }
 }
 
-// The 32 MFMAs of one stage.
-template <typename T>
-__device__ inline void stage_mma(const FragSet<T>& f, f32x16 (&acc)[FP][FQ]) {
+// The 2 F^2 MFMAs of one stage.
+template <typename T, int F>
+__device__ inline void stage_mma(const FragSet<T, F>& f, f32x16 (&acc)[F][F]) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int i = 0; i < FP; ++i)
+    for (int i = 0; i < F; ++i)
 #pragma unroll
-      for (int j = 0; j < FQ; ++j) acc[i][j] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j], acc[i][j]);
+      for (int j = 0; j < F; ++j) acc[i][j] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j], acc[i][j]);
 }
 
 // Swap a value with the neighbouring lane (lane ^ 1): DPP quad_perm [1, 0, 3, 2].
@@ -292,16 +311,16 @@ template <> __device__ inline float2 unpack2<fp16>(uint32_t v) {
 // swap with the neighbouring lane, even lanes hold (row R, columns c, c + 1) and odd
 // lanes (row R + 1, columns c - 1, c).  fn(row, col, lo, hi) gets tile-local
 // coordinates (row, col even).
-template <typename Fn>
-__device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane_in, Fn&& fn) {
+template <int F, typename Fn>
+__device__ inline void for_each_pair(const f32x16 (&acc)[F][F], int lane_in, Fn&& fn) {
   int lane = lane_in;
   asm volatile("" : "+v"(lane));   // per-lane terms are formed here, not hoisted out of the
                                    // tile loop (they would stay live, and spill)
   const int odd = lane & 1;
 #pragma unroll
-  for (int i = 0; i < FP; ++i)
+  for (int i = 0; i < F; ++i)
 #pragma unroll
-    for (int j = 0; j < FQ; ++j)
+    for (int j = 0; j < F; ++j)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
@@ -313,24 +332,24 @@ __device__ inline void for_each_pair(const f32x16 (&acc)[FP][FQ], int lane_in, F
       }
 }
 
-// dW[row, col] += accumulators of block row I (32 rows of the wave's 128), for a tile
+// dW[row, col] += accumulators of block row I (32 rows of the wave's WR), for a tile
 // without an M split.  `r` is a buffer window over the wave's valid dW rows (rows past K
 // are dropped by the range check); columns past N are pushed out of the window
 // (cols_left: columns left from the wave's first).  The old values of all of the block's
 // pairs are loaded before any of them is stored: the compiler cannot move a load of dW
 // above a store to dW, so a load-add-store per pair would cost one memory round trip each
-// (128 per wave); batched, the wave makes four.  Offsets are 32-bit (128 rows of < 2^23
-// bytes).
-template <typename T, int I>
-__device__ inline void rmw_block_rows(const f32x16 (&acc)[FP][FQ], int lane,
+// (128 per wave at F = 4); batched, the wave makes F.  Offsets are 32-bit (128 rows of
+// < 2^23 bytes).
+template <typename T, int F, int I>
+__device__ inline void rmw_block_rows(const f32x16 (&acc)[F][F], int lane,
                                       __amdgpu_buffer_rsrc_t r, uint32_t row_bytes,
                                       int cols_left) {
   const int odd = lane & 1;
   const uint32_t loff = (uint32_t)(4 * (lane >> 5) + odd) * row_bytes +
                         (uint32_t)((lane & 31) & ~1) * 2u;
-  uint32_t voff[FQ][8], old[FQ][8];
+  uint32_t voff[F][8], old[F][8];
 #pragma unroll
-  for (int j = 0; j < FQ; ++j) {
+  for (int j = 0; j < F; ++j) {
     const uint32_t cbad = j * 32 + ((lane & 31) & ~1) < cols_left ? 0u : kOOB;
 #pragma unroll
     for (int r2 = 0; r2 < 8; ++r2) {
@@ -341,7 +360,7 @@ __device__ inline void rmw_block_rows(const f32x16 (&acc)[FP][FQ], int lane,
     }
   }
 #pragma unroll
-  for (int j = 0; j < FQ; ++j)
+  for (int j = 0; j < F; ++j)
 #pragma unroll
     for (int r2 = 0; r2 < 8; ++r2) {
       const int rr = 2 * r2;
@@ -363,8 +382,8 @@ __device__ inline void rmw_block_rows(const f32x16 (&acc)[FP][FQ], int lane,
 // from the tile's first; a multiple of 8, so a pair never straddles it).  wrow0 / wcol0:
 // the wave's first row / column inside the tile.  All offsets are 32-bit (256 rows x 2^23
 // bytes < 2^31).
-template <typename T>
-__device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
+template <typename T, int F>
+__device__ inline void store_tile_rows(const f32x16 (&acc)[F][F], int lane,
                                        __amdgpu_buffer_rsrc_t r, uint32_t row_bytes, int wrow0,
                                        int wcol0, int cols_left) {
   const int odd = lane & 1;
@@ -375,9 +394,9 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
                                    // the tile loop (they would stay live, and spill)
   // columns past the tensor's edge: the offset is pushed past the window and the store is
   // dropped by the range check (no branch per store)
-  uint32_t cbad[FQ];
+  uint32_t cbad[F];
 #pragma unroll
-  for (int j = 0; j < FQ; ++j) {
+  for (int j = 0; j < F; ++j) {
     cbad[j] = wcol0 + j * 32 + ((lane & 31) & ~1) < cols_left ? 0u : kOOB;
     asm volatile("" : "+v"(cbad[j]));   // formed here, not hoisted (see loff)
   }
@@ -388,7 +407,7 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
   int go = 1;
   asm volatile("" : "+s"(go));
 #pragma unroll
-  for (int i = 0; i < FP; ++i) {
+  for (int i = 0; i < F; ++i) {
 #pragma unroll
     for (int rr = 0; rr < 16; rr += 2) {
       asm volatile("" : "+s"(go));   // a fresh value per block (no threading of the tests)
@@ -396,7 +415,7 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[FP][FQ], int lane,
         const uint32_t voff =
             loff + (uint32_t)(wrow0 + i * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes;
 #pragma unroll
-        for (int j = 0; j < FQ; ++j) {
+        for (int j = 0; j < F; ++j) {
           const uint32_t own = pack2<T>(acc[i][j][rr], acc[i][j][rr + 1]);
           const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
           const uint32_t out = __builtin_amdgcn_perm(nb, own, sel);
@@ -439,12 +458,13 @@ struct XTile {   // first row of the dg/dfc panel and of the W panel; 32-bit (M 
   bool live;
 };
 
+template <int F>
 __device__ inline XTile x_tile(int64_t L, bool live, int64_t nq) {
   XTile c;
   c.live = live;
   const int64_t LL = live ? L : 0;
-  c.p0 = (int)(LL / nq) * BP;
-  c.q0 = (int)(LL % nq) * BQ;
+  c.p0 = (int)(LL / nq) * Tc<F>::P;
+  c.q0 = (int)(LL % nq) * Tc<F>::P;
   return c;
 }
 
@@ -464,10 +484,12 @@ struct XWin {
   uint32_t a_bytes, b_bytes;
 };
 
+template <int F>
 __device__ inline XWin x_win(const XTile& c, int64_t M, int64_t K, int64_t N) {
   XWin w;
-  const int64_t ra = c.live ? (M - c.p0 < BP ? M - c.p0 : BP) : 0;
-  const int64_t rb = c.live ? (K - c.q0 < BQ ? K - c.q0 : BQ) : 0;
+  constexpr int P = Tc<F>::P;
+  const int64_t ra = c.live ? (M - c.p0 < P ? M - c.p0 : P) : 0;
+  const int64_t rb = c.live ? (K - c.q0 < P ? K - c.q0 : P) : 0;
   w.a_off = (int64_t)c.p0 * N;
   w.b_off = (int64_t)c.q0 * N;
   w.a_bytes = (uint32_t)(ra * N * 2);
@@ -502,84 +524,90 @@ __device__ inline XIssue x_issue(const T* lo, const T* hi_arr, XWin wc, XWin wn,
   return is;
 }
 
-// This lane's voffset for load i (0..7) of an issue.
-template <bool RAGGED>
-__device__ inline uint32_t x_voff(const XIssue& is, const uint32_t (&aoff)[8], const int (&acol)[2],
+// This lane's voffset for load i (0 .. 2F - 1) of an issue.
+template <bool RAGGED, int L>
+__device__ inline uint32_t x_voff(const XIssue& is, const uint32_t (&aoff)[L], const int (&acol)[2],
                                   int i) {
   if (!RAGGED) return aoff[i];
   return acol[i & 1] < is.lim ? aoff[i] : kOOB;
 }
 
-
-template <bool RAGGED>
-__device__ inline void x_issue_all(const XIssue& is, const uint32_t (&aoff)[8],
-                                   const int (&acol)[2]) {
-  dma16s<0 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 0), is.soff, is.dst);
-  dma16s<1 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 1), is.soff, is.dst);
-  dma16s<2 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 2), is.soff, is.dst);
-  dma16s<3 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 3), is.soff, is.dst);
-  dma16s<4 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 4), is.soff, is.dst);
-  dma16s<5 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 5), is.soff, is.dst);
-  dma16s<6 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 6), is.soff, is.dst);
-  dma16s<7 * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, 7), is.soff, is.dst);
+template <bool RAGGED, int L, int... I>
+__device__ inline void x_issue_loads(std::integer_sequence<int, I...>, const XIssue& is,
+                                     const uint32_t (&aoff)[L], const int (&acol)[2]) {
+  (dma16s<I * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, I), is.soff, is.dst), ...);
 }
 
-// Fragment G (0..15, in x_read's order: kk = G / 8; G % 8 < 4: A block G % 4, else B
-// block G % 4) of stage half HALF.
-template <typename T, int HALF, int G>
+template <bool RAGGED, int L>
+__device__ inline void x_issue_all(const XIssue& is, const uint32_t (&aoff)[L],
+                                   const int (&acol)[2]) {
+  x_issue_loads<RAGGED>(std::make_integer_sequence<int, L>{}, is, aoff, acol);
+}
+
+// Fragment G (0 .. 4F - 1, in x_read's order: kk = G / 2F; G % 2F < F: A block G % 2F,
+// else B block G % 2F - F) of stage half HALF.
+template <typename T, int F, int HALF, int G>
 __device__ inline void x_read_one(const uint16_t* aslot, const uint16_t* bslot, int wp, int wq,
-                                  int lane, FragSet<T>& f) {
-  using F = typename Mfma<T>::frag;
-  constexpr int kk = G / 8, blk = G % 4;
+                                  int lane, FragSet<T, F>& f) {
+  using Fr = typename Mfma<T>::frag;
+  constexpr int kk = G / (2 * F), idx = G % (2 * F);
   const int lc = 2 * kk + (lane >> 5);
-  if (G % 8 < 4) {
-    const int r = wp * 128 + blk * 32 + (lane & 31);
-    f.a[kk][blk] = *reinterpret_cast<const F*>(aslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
+  if (idx < F) {
+    const int r = wp * Tc<F>::WR + idx * 32 + (lane & 31);
+    f.a[kk][idx] = *reinterpret_cast<const Fr*>(aslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
   } else {
-    const int r = wq * 128 + blk * 32 + (lane & 31);
-    f.b[kk][blk] = *reinterpret_cast<const F*>(bslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
+    const int r = wq * Tc<F>::WR + (idx - F) * 32 + (lane & 31);
+    f.b[kk][idx - F] = *reinterpret_cast<const Fr*>(bslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
   }
 }
 
-// Group G of an odd step: MFMAs 2G, 2G + 1 of the stage in f (stage_mma's order), fragment
-// G of the next stage (READ_NEXT), and load G % 8 of the B issue (G < 8) or of the A issue.
-// The scheduling fence keeps the groups in this order, so that the 16 loads and the
-// address work around them are spread over the step instead of stalling the matrix cores
-// behind the barrier.
-template <typename T, bool RAGGED, bool READ_NEXT, int G>
-__device__ inline void x_odd_group(f32x16 (&acc)[FP][FQ], const FragSet<T>& f, FragSet<T>& fn,
-                                   const uint16_t* aslot, const uint16_t* bslot, int wp, int wq,
-                                   int lane, const XIssue& is, const uint32_t (&aoff)[8],
-                                   const int (&acol)[2]) {
-  constexpr int kk = G >> 3, i = (G >> 1) & 3, j = (G & 1) * 2;
+// MFMA q (stage_mma's order) of the stage in f.
+template <typename T, int F, int Q>
+__device__ inline void mma_q(f32x16 (&acc)[F][F], const FragSet<T, F>& f) {
+  constexpr int kk = Q / (F * F), i = (Q / F) % F, j = Q % F;
   acc[i][j] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j], acc[i][j]);
-  acc[i][j + 1] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j + 1], acc[i][j + 1]);
-  if (READ_NEXT) x_read_one<T, 0, G>(aslot, bslot, wp, wq, lane, fn);
-  dma16s<(G & 7) * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, G & 7), is.soff, is.dst);
+}
+
+// Group G (0 .. 4F - 1) of an odd step: MFMAs F/2 G .. F/2 G + F/2 - 1 of the stage in f
+// (stage_mma's order), fragment G of the next stage (READ_NEXT), and load G % 2F of the B
+// issue (G < 2F) or of the A issue.  The scheduling fence keeps the groups in this order,
+// so that the 4F loads and the address work around them are spread over the step instead
+// of stalling the matrix cores behind the barrier.
+template <typename T, int F, bool RAGGED, bool READ_NEXT, int G>
+__device__ inline void x_odd_group(f32x16 (&acc)[F][F], const FragSet<T, F>& f,
+                                   FragSet<T, F>& fn, const uint16_t* aslot,
+                                   const uint16_t* bslot, int wp, int wq, int lane,
+                                   const XIssue& is, const uint32_t (&aoff)[2 * F],
+                                   const int (&acol)[2]) {
+  mma_q<T, F, G * (F / 2)>(acc, f);
+  if constexpr (F == 4) mma_q<T, F, G * (F / 2) + 1>(acc, f);
+  if (READ_NEXT) x_read_one<T, F, 0, G>(aslot, bslot, wp, wq, lane, fn);
+  constexpr int e = G % (2 * F);
+  dma16s<e * 1024>(is.r, x_voff<RAGGED>(is, aoff, acol, e), is.soff, is.dst);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename T, bool RAGGED, bool READ_NEXT, int... G>
-__device__ inline void x_odd_groups(std::integer_sequence<int, G...>, f32x16 (&acc)[FP][FQ],
-                                    const FragSet<T>& f, FragSet<T>& fn, const uint16_t* aslot,
-                                    const uint16_t* bslot, int wp, int wq, int lane,
-                                    const XIssue& is, const uint32_t (&aoff)[8],
+template <typename T, int F, bool RAGGED, bool READ_NEXT, int OFS, int... G>
+__device__ inline void x_odd_groups(std::integer_sequence<int, G...>, f32x16 (&acc)[F][F],
+                                    const FragSet<T, F>& f, FragSet<T, F>& fn,
+                                    const uint16_t* aslot, const uint16_t* bslot, int wp, int wq,
+                                    int lane, const XIssue& is, const uint32_t (&aoff)[2 * F],
                                     const int (&acol)[2]) {
-  (x_odd_group<T, RAGGED, READ_NEXT, G>(acc, f, fn, aslot, bslot, wp, wq, lane, is, aoff, acol),
+  (x_odd_group<T, F, RAGGED, READ_NEXT, OFS + G>(acc, f, fn, aslot, bslot, wp, wq, lane, is,
+                                                 aoff, acol),
    ...);
 }
-using XGroupsB = std::integer_sequence<int, 0, 1, 2, 3, 4, 5, 6, 7>;
-using XGroupsA = std::integer_sequence<int, 8, 9, 10, 11, 12, 13, 14, 15>;
 
 // The x-stage tile walk of one workgroup: tiles f0, f0 + G, f0 + 2G, ... of the ntiles
 // output tiles, through the LDS ring at `ring` (3 A slots then 2 B slots).
-template <typename T, bool RAGGED>
+template <typename T, int F, bool RAGGED>
 __device__ __attribute__((always_inline)) inline void x_tiles(
     uint16_t* ring, const T* __restrict__ dg, const T* __restrict__ dfc,
     const T* __restrict__ wg, const T* __restrict__ wfc, T* __restrict__ dx, int64_t M,
     int64_t K, int64_t N, int64_t nq, int64_t ntiles, int64_t f0, int64_t G) {
+  constexpr int P = Tc<F>::P, XSLOT = Tc<F>::XSLOT, XLOADS = Tc<F>::XLOADS;
   uint16_t* const ra0 = ring;
-  uint16_t* const rb0 = ring + 3 * XA_SLOT;
+  uint16_t* const rb0 = ring + 3 * XSLOT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / WQ, wq = wave % WQ;
@@ -590,21 +618,21 @@ __device__ __attribute__((always_inline)) inline void x_tiles(
   if (sD < 2) sD = 2;
   const int nds = 2 * sD;                          // double stages per tile (even, >= 4)
 
-  // A and B alike: a 1 KiB load covers 8 rows x 8 chunks, rows 64 wave + 8 i + lane / 8
-  // (i = 0..7); the lane fetches the logical chunk that its LDS position holds under the
-  // swizzle.  xsw8(64 wave + 8 i + lane / 8) = (4 i + lane / 16) % 8, so the column term
-  // takes two values per lane; dg, dfc, W_g and W_fc all have rows of N elements, so the
-  // offsets serve both operands.
-  uint32_t aoff[8];
+  // A and B alike: a 1 KiB load covers 8 rows x 8 chunks, rows P / 4 wave + 8 i + lane / 8
+  // (i = 0 .. 2F - 1); the lane fetches the logical chunk that its LDS position holds under
+  // the swizzle.  xsw8(P / 4 wave + 8 i + lane / 8) = (4 i + lane / 16) % 8, so the column
+  // term takes two values per lane; dg, dfc, W_g and W_fc all have rows of N elements, so
+  // the offsets serve both operands.
+  uint32_t aoff[XLOADS];
   int acol[2];
   acol[0] = ((lane & 7) ^ ((lane >> 4) & 7)) * 8;
   acol[1] = ((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 64 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < XLOADS; ++i) {
+    const int row = (P / 4) * wave + 8 * i + (lane >> 3);
     aoff[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)acol[i & 1] * 2u;
   }
-  const int wofs = 64 * wave * XA_BR;   // this wave's rows in a slot
+  const int wofs = (P / 4) * wave * XA_BR;   // this wave's rows in a slot
   auto issue_a = [&](XWin wc, XWin wn, int d, uint16_t* slot) {
     asm volatile("" : "+s"(d));   // keep per-stage values from being hoisted (they would
                                   // stay live across the tile loop, and spill)
@@ -614,62 +642,64 @@ __device__ __attribute__((always_inline)) inline void x_tiles(
     asm volatile("" : "+s"(d));
     return x_issue<T>(wg, wfc, wc, wn, false, d, nds, sD, N, slot + wofs);
   };
-#define X_READ(h, as, bs, f) x_read<T, (h)>((as), (bs), wp, wq, lane, (f))
+#define X_READ(h, as, bs, f) x_read<T, F, (h)>((as), (bs), wp, wq, lane, (f))
   // even step: second halves of the current double stage
 #define X_STEP_EVEN()                                                                     \
   do {                                                                                    \
-    X_READ(1, ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, frags[1]);                           \
-    stage_mma<T>(frags[0], acc);                                                          \
-    step_schedule<16>();                                                                  \
+    X_READ(1, ra0 + as * XSLOT, rb0 + bs * XSLOT, frags[1]);                               \
+    stage_mma<T, F>(frags[0], acc);                                                       \
+    step_schedule<2 * F * F, 4 * F>();                                                    \
   } while (0)
   // odd step t = 2d + 1 (d = t0 / 2 + (u - 1) / 2); READ_NEXT = 0 on the last step of a tile
 #define X_STEP_ODD(d, READ_NEXT)                                                           \
   do {                                                                                    \
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(XA_LOADS));                                       \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(XLOADS));                                         \
     __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                                \
     SWG_COMPILER_FENCE();                                                                 \
     __builtin_amdgcn_s_barrier();                                                         \
     SWG_COMPILER_FENCE();                                                                 \
-    uint16_t* const bfree_ = rb0 + bs * XB_SLOT;                                          \
-    uint16_t* const afree_ = ra0 + as * XA_SLOT;                                          \
+    uint16_t* const bfree_ = rb0 + bs * XSLOT;                                            \
+    uint16_t* const afree_ = ra0 + as * XSLOT;                                            \
     as = (as == 2 ? 0 : as + 1);                                                          \
     bs ^= 1;                                                                              \
     const XIssue ib_ = issue_b(wc, wn, (d) + 2, bfree_);                                   \
-    x_odd_groups<T, RAGGED, (READ_NEXT)>(XGroupsB{}, acc, frags[1], frags[0],              \
-                                         ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, wp, wq,   \
-                                         lane, ib_, aoff, acol);                          \
+    x_odd_groups<T, F, RAGGED, (READ_NEXT), 0>(std::make_integer_sequence<int, 2 * F>{},   \
+                                               acc, frags[1], frags[0], ra0 + as * XSLOT,  \
+                                               rb0 + bs * XSLOT, wp, wq, lane, ib_, aoff,  \
+                                               acol);                                     \
     const XIssue ia_ = issue_a(wc, wn, (d) + 3, afree_);                                   \
-    x_odd_groups<T, RAGGED, (READ_NEXT)>(XGroupsA{}, acc, frags[1], frags[0],              \
-                                         ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, wp, wq,   \
-                                         lane, ia_, aoff, acol);                          \
+    x_odd_groups<T, F, RAGGED, (READ_NEXT), 2 * F>(std::make_integer_sequence<int, 2 * F>{}, \
+                                                   acc, frags[1], frags[0],                \
+                                                   ra0 + as * XSLOT, rb0 + bs * XSLOT, wp, \
+                                                   wq, lane, ia_, aoff, acol);            \
   } while (0)
 
-  f32x16 acc[FP][FQ];
-  FragSet<T> frags[2];
-  XTile nxt = x_tile(f0 + G, my_tiles > 1, nq);
-  XWin wc = x_win(x_tile(f0, my_tiles > 0, nq), M, K, N);
-  XWin wn = x_win(nxt, M, K, N);
+  f32x16 acc[F][F];
+  FragSet<T, F> frags[2];
+  XTile nxt = x_tile<F>(f0 + G, my_tiles > 1, nq);
+  XWin wc = x_win<F>(x_tile<F>(f0, my_tiles > 0, nq), M, K, N);
+  XWin wn = x_win<F>(nxt, M, K, N);
   int as = 0, bs = 0;   // A and B slots of the double stage holding the current stage
   // prologue, in the steady-state issue order: A0 B0 A1 B1 A2
   x_issue_all<RAGGED>(issue_a(wc, wn, 0, ra0), aoff, acol);
   x_issue_all<RAGGED>(issue_b(wc, wn, 0, rb0), aoff, acol);
-  x_issue_all<RAGGED>(issue_a(wc, wn, 1, ra0 + XA_SLOT), aoff, acol);
-  x_issue_all<RAGGED>(issue_b(wc, wn, 1, rb0 + XB_SLOT), aoff, acol);
-  x_issue_all<RAGGED>(issue_a(wc, wn, 2, ra0 + 2 * XA_SLOT), aoff, acol);
-  __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * XA_LOADS + XB_LOADS));   // A0 and B0 landed
+  x_issue_all<RAGGED>(issue_a(wc, wn, 1, ra0 + XSLOT), aoff, acol);
+  x_issue_all<RAGGED>(issue_b(wc, wn, 1, rb0 + XSLOT), aoff, acol);
+  x_issue_all<RAGGED>(issue_a(wc, wn, 2, ra0 + 2 * XSLOT), aoff, acol);
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * XLOADS));   // A0 and B0 landed
   SWG_COMPILER_FENCE();
   __builtin_amdgcn_s_barrier();
   SWG_COMPILER_FENCE();
   for (int64_t j = 0; j < my_tiles; ++j) {
-    const XTile cur = x_tile(f0 + j * G, true, nq);
+    const XTile cur = x_tile<F>(f0 + j * G, true, nq);
     if (j > 0) {
-      nxt = x_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
+      nxt = x_tile<F>(f0 + (j + 1) * G, j + 1 < my_tiles, nq);
       wc = wn;
-      wn = x_win(nxt, M, K, N);
+      wn = x_win<F>(nxt, M, K, N);
     }
     __builtin_amdgcn_sched_barrier(0);   // the epilogue stays ahead of the next reads
     zero_acc(acc);
-    X_READ(0, ra0 + as * XA_SLOT, rb0 + bs * XB_SLOT, frags[0]);   // stage 0
+    X_READ(0, ra0 + as * XSLOT, rb0 + bs * XSLOT, frags[0]);   // stage 0
     int d0 = 0;
     for (; d0 + 2 < nds; d0 += 2) {
       X_STEP_EVEN();
@@ -683,10 +713,10 @@ __device__ __attribute__((always_inline)) inline void x_tiles(
     X_STEP_ODD(d0 + 1, false);
     // epilogue: straight from the accumulators, two adjacent columns per 32-bit store
     {
-      const int rows = (int)M - cur.p0 < BP ? (int)M - cur.p0 : BP;
-      store_tile_rows<T>(acc, lane,
-                         make_rsrc(dx + (int64_t)cur.p0 * K + cur.q0, clamp_bytes(rows, K * 2)),
-                         (uint32_t)(K * 2), wp * 128, wq * 128, (int)K - cur.q0);
+      const int rows = (int)M - cur.p0 < P ? (int)M - cur.p0 : P;
+      store_tile_rows<T, F>(acc, lane,
+                            make_rsrc(dx + (int64_t)cur.p0 * K + cur.q0, clamp_bytes(rows, K * 2)),
+                            (uint32_t)(K * 2), wp * Tc<F>::WR, wq * Tc<F>::WR, (int)K - cur.q0);
     }
   }
 #undef X_STEP_EVEN
@@ -695,17 +725,15 @@ __device__ __attribute__((always_inline)) inline void x_tiles(
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
-constexpr int X_RING_ELEMS = 3 * XA_SLOT + 2 * XB_SLOT;   // 160 KiB
-
-template <typename T, bool RAGGED>
+template <typename T, int F, bool RAGGED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void x_stage_kernel(
     const T* __restrict__ dg, const T* __restrict__ dfc, const T* __restrict__ wg,
     const T* __restrict__ wfc, T* __restrict__ dx, int64_t M, int64_t K, int64_t N, int64_t nq,
     int64_t ntiles) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[X_RING_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[Tc<F>::X_RING];
   const int64_t G = gridDim.x;
-  x_tiles<T, RAGGED>(ring, dg, dfc, wg, wfc, dx, M, K, N, nq, ntiles,
-                     xcd_remap(blockIdx.x, G), G);
+  x_tiles<T, F, RAGGED>(ring, dg, dfc, wg, wfc, dx, M, K, N, nq, ntiles,
+                        xcd_remap(blockIdx.x, G), G);
 }
 
 // ----------------------------------------------------------------- w stage (TN)
@@ -728,6 +756,7 @@ struct WMap {          // how items map to rows (see WItem)
   int64_t nsplit;      // S
 };
 
+template <int F>
 __device__ inline WItem w_item(int64_t L, bool live, int64_t tiles, int64_t tnh,
                                const WMap& mp, int64_t M) {
   WItem w;
@@ -737,8 +766,8 @@ __device__ inline WItem w_item(int64_t L, bool live, int64_t tiles, int64_t tnh,
   const int tt = (int)(LL % tiles);
   const int kb = tt / (int)(2 * tnh), nb = tt % (int)(2 * tnh);
   w.hi = nb >= tnh;
-  w.k0 = kb * BP;
-  w.n0 = (w.hi ? nb - (int)tnh : nb) * BQ;
+  w.k0 = kb * Tc<F>::P;
+  w.n0 = (w.hi ? nb - (int)tnh : nb) * Tc<F>::P;
   if (mp.split_rows > 0) {
     w.m_begin = w.s * (int)mp.split_rows;
     w.m_end = (w.m_begin + mp.split_rows < M) ? w.m_begin + (int)mp.split_rows : (int)M;
@@ -774,72 +803,75 @@ struct WIssue {
   const uint16_t* dst;
 };
 
-// Load e (0..7) of a w-stage issue: e < 4 fetches rows of x, e >= 4 rows of dg / dfc.
-template <bool RAGGED, int E>
-__device__ inline void w_dma(const WIssue& is, const uint32_t (&xbase)[4],
-                             const uint32_t (&dbase)[4], const int (&lcol)[4]) {
-  constexpr int i = E & 3;
-  if (E < 4) {
+// Load e (0 .. 2F - 1) of a w-stage issue: e < F fetches rows of x, e >= F rows of
+// dg / dfc; each load is 1 KiB of the wave's part of the slot.
+template <bool RAGGED, int F, int E>
+__device__ inline void w_dma(const WIssue& is, const uint32_t (&xbase)[F],
+                             const uint32_t (&dbase)[F], const int (&lcol)[F]) {
+  constexpr int i = E % F;
+  if (E < F) {
     const uint32_t v = !RAGGED || lcol[i] < is.kleft ? xbase[i] : kOOB;
-    dma16s<i * 2 * BP * 2>(is.rx, v, is.sx, is.dst);
+    dma16s<i * 1024>(is.rx, v, is.sx, is.dst);
   } else {
     const uint32_t v = !RAGGED || lcol[i] < is.nleft ? dbase[i] : kOOB;
-    dma16s<BR * BP * 2 + i * 2 * BP * 2>(is.rd, v, is.sd, is.dst);
+    dma16s<BR * Tc<F>::P * 2 + i * 1024>(is.rd, v, is.sd, is.dst);
   }
 }
 
-template <bool RAGGED>
-__device__ inline void w_issue_all(const WIssue& is, const uint32_t (&xbase)[4],
-                                   const uint32_t (&dbase)[4], const int (&lcol)[4]) {
-  w_dma<RAGGED, 0>(is, xbase, dbase, lcol);
-  w_dma<RAGGED, 1>(is, xbase, dbase, lcol);
-  w_dma<RAGGED, 2>(is, xbase, dbase, lcol);
-  w_dma<RAGGED, 3>(is, xbase, dbase, lcol);
-  w_dma<RAGGED, 4>(is, xbase, dbase, lcol);
-  w_dma<RAGGED, 5>(is, xbase, dbase, lcol);
-  w_dma<RAGGED, 6>(is, xbase, dbase, lcol);
-  w_dma<RAGGED, 7>(is, xbase, dbase, lcol);
+template <bool RAGGED, int F, int... E>
+__device__ inline void w_issue_loads(std::integer_sequence<int, E...>, const WIssue& is,
+                                     const uint32_t (&xbase)[F], const uint32_t (&dbase)[F],
+                                     const int (&lcol)[F]) {
+  (w_dma<RAGGED, F, E>(is, xbase, dbase, lcol), ...);
 }
 
-// Fragment G (0..15, w_read's order) of a w-stage slot.
-template <typename T, int G>
-__device__ inline void w_read_one(const uint16_t* slot, const int (&aoff)[FP],
-                                  const int (&boff)[FQ], FragSet<T>& f) {
-  constexpr int ks = G / 8, blk = G % 4;
-  if (G % 8 < 4) f.a[ks][blk] = w_frag<T>(slot + 16 * ks * BQ + aoff[blk]);
-  else f.b[ks][blk] = w_frag<T>(slot + BR * BP + 16 * ks * BQ + boff[blk]);
+template <bool RAGGED, int F>
+__device__ inline void w_issue_all(const WIssue& is, const uint32_t (&xbase)[F],
+                                   const uint32_t (&dbase)[F], const int (&lcol)[F]) {
+  w_issue_loads<RAGGED, F>(std::make_integer_sequence<int, 2 * F>{}, is, xbase, dbase, lcol);
 }
 
-// Group G of a w step: MFMAs 2G, 2G + 1 of the stage in f, fragment G of the next stage
-// (READ_NEXT) and, in odd groups, load G / 2 of the issue, kept in this order by the
-// scheduling fence (see x_odd_group).
-template <typename T, bool RAGGED, bool READ_NEXT, int G>
-__device__ inline void w_group(f32x16 (&acc)[FP][FQ], const FragSet<T>& f, FragSet<T>& fn,
-                               const uint16_t* next_slot, const int (&aoff)[FP],
-                               const int (&boff)[FQ], const WIssue& is,
-                               const uint32_t (&xbase)[4], const uint32_t (&dbase)[4],
-                               const int (&lcol)[4]) {
-  constexpr int kk = G >> 3, i = (G >> 1) & 3, j = (G & 1) * 2;
-  acc[i][j] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j], acc[i][j]);
-  acc[i][j + 1] = Mfma<T>::mma(f.a[kk][i], f.b[kk][j + 1], acc[i][j + 1]);
-  if (READ_NEXT) w_read_one<T, G>(next_slot, aoff, boff, fn);
-  if (G & 1) w_dma<RAGGED, (G >> 1)>(is, xbase, dbase, lcol);
+// Fragment G (0 .. 4F - 1, w_read's order) of a w-stage slot.
+template <typename T, int F, int G>
+__device__ inline void w_read_one(const uint16_t* slot, const int (&aoff)[F],
+                                  const int (&boff)[F], FragSet<T, F>& f) {
+  constexpr int P = Tc<F>::P;
+  constexpr int ks = G / (2 * F), idx = G % (2 * F);
+  if (idx < F) f.a[ks][idx] = tr_frag<T, P>(slot + 16 * ks * P + aoff[idx]);
+  else f.b[ks][idx - F] = tr_frag<T, P>(slot + BR * P + 16 * ks * P + boff[idx - F]);
+}
+
+// Group G (0 .. 4F - 1) of a w step: MFMAs F/2 G .. F/2 G + F/2 - 1 of the stage in f,
+// fragment G of the next stage (READ_NEXT) and, in odd groups, load G / 2 of the issue,
+// kept in this order by the scheduling fence (see x_odd_group).
+template <typename T, int F, bool RAGGED, bool READ_NEXT, int G>
+__device__ inline void w_group(f32x16 (&acc)[F][F], const FragSet<T, F>& f, FragSet<T, F>& fn,
+                               const uint16_t* next_slot, const int (&aoff)[F],
+                               const int (&boff)[F], const WIssue& is,
+                               const uint32_t (&xbase)[F], const uint32_t (&dbase)[F],
+                               const int (&lcol)[F]) {
+  mma_q<T, F, G * (F / 2)>(acc, f);
+  if constexpr (F == 4) mma_q<T, F, G * (F / 2) + 1>(acc, f);
+  if (READ_NEXT) w_read_one<T, F, G>(next_slot, aoff, boff, fn);
+  if constexpr ((G & 1) != 0) w_dma<RAGGED, F, (G >> 1)>(is, xbase, dbase, lcol);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename T, bool RAGGED, bool READ_NEXT, int... G>
-__device__ inline void w_groups(std::integer_sequence<int, G...>, f32x16 (&acc)[FP][FQ],
-                                const FragSet<T>& f, FragSet<T>& fn, const uint16_t* next_slot,
-                                const int (&aoff)[FP], const int (&boff)[FQ], const WIssue& is,
-                                const uint32_t (&xbase)[4], const uint32_t (&dbase)[4],
-                                const int (&lcol)[4]) {
-  (w_group<T, RAGGED, READ_NEXT, G>(acc, f, fn, next_slot, aoff, boff, is, xbase, dbase, lcol),
+template <typename T, int F, bool RAGGED, bool READ_NEXT, int... G>
+__device__ inline void w_groups(std::integer_sequence<int, G...>, f32x16 (&acc)[F][F],
+                                const FragSet<T, F>& f, FragSet<T, F>& fn,
+                                const uint16_t* next_slot, const int (&aoff)[F],
+                                const int (&boff)[F], const WIssue& is,
+                                const uint32_t (&xbase)[F], const uint32_t (&dbase)[F],
+                                const int (&lcol)[F]) {
+  (w_group<T, F, RAGGED, READ_NEXT, G>(acc, f, fn, next_slot, aoff, boff, is, xbase, dbase,
+                                       lcol),
    ...);
 }
 
 // The w-stage item walk of one workgroup: items f0, f0 + G, ... of the nitems items,
 // through the LDS ring at `ring` (four slots).
-template <typename T, bool RAGGED>
+template <typename T, int F, bool RAGGED>
 __device__ __attribute__((always_inline)) inline void w_items(
     uint16_t* ring, const T* __restrict__ x, const T* __restrict__ dg,
     const T* __restrict__ dfc, T* __restrict__ dwg, T* __restrict__ dwfc,
@@ -849,17 +881,20 @@ __device__ __attribute__((always_inline)) inline void w_items(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / WQ, wq = wave % WQ;
   const int64_t my_items = nitems > f0 ? (nitems - f0 + G - 1) / G : 0;
+  constexpr int P = Tc<F>::P, WR = Tc<F>::WR, WSLOT = Tc<F>::WSLOT, WLOADS = Tc<F>::WLOADS;
+  constexpr int RPL = Tc<F>::RPL, LPR = 64 / RPL;   // rows per load, lanes per row
 
-  // A 1 KiB load covers 2 rows x 32 chunks; this wave's loads are rows 8 wave + 2 i +
-  // lane / 32 (i = 0..3) of A and of B, logical chunk (lane % 32) ^ wsw(row).  The lane
-  // parts of the offsets are fixed; the tile adds k0 / n0 (uniform).  One buffer window
-  // per stage: rows m0 .. m0 + 32 (rows past m_end, and every row of a dead item, read 0).
-  uint32_t xbase[4], dbase[4];
-  int lcol[4];
+  // A 1 KiB load covers RPL rows x P / 8 chunks; this wave's loads are rows 8 wave +
+  // RPL i + lane / LPR (i = 0 .. F - 1) of A and of B, logical chunk (lane % LPR) ^
+  // wsw(row).  The lane parts of the offsets are fixed; the tile adds k0 / n0 (uniform).
+  // One buffer window per stage: rows m0 .. m0 + 32 (rows past m_end, and every row of a
+  // dead item, read 0).
+  uint32_t xbase[F], dbase[F];
+  int lcol[F];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 8 * wave + 2 * i + (lane >> 5);
-    lcol[i] = ((lane & 31) ^ wsw(row)) * 8;
+  for (int i = 0; i < F; ++i) {
+    const int row = 8 * wave + RPL * i + lane / LPR;
+    lcol[i] = ((lane % LPR) ^ wsw(row)) * 8;
     xbase[i] = (uint32_t)row * (uint32_t)(K * 2) + (uint32_t)lcol[i] * 2u;
     dbase[i] = (uint32_t)row * (uint32_t)(N * 2) + (uint32_t)lcol[i] * 2u;
   }
@@ -877,18 +912,14 @@ __device__ __attribute__((always_inline)) inline void w_items(
     is.sd = __builtin_amdgcn_readfirstlane((uint32_t)w.n0 * 2u);
     is.kleft = (int)K - w.k0;   // columns left in the tile
     is.nleft = (int)N - w.n0;
-    is.dst = slot + 8 * wave * BP;   // this wave's 4 row pairs
+    is.dst = slot + 8 * wave * P;   // this wave's 8 rows
     return is;
   };
 
-  int aoff[FP], boff[FQ];
-  w_lane_offsets(lane, aoff);
-#pragma unroll
-  for (int i = 0; i < FP; ++i) {
-    boff[i] = aoff[i] + wq * 128;
-    aoff[i] += wp * 128;
-  }
-#define W_READ(slot, f) w_read<T>((slot), aoff, boff, (f))
+  int aoff[F], boff[F];
+  w_lane_offsets<F, P>(lane, wp * (WR / 8), aoff);
+  w_lane_offsets<F, P>(lane, wq * (WR / 8), boff);
+#define W_READ(slot, f) w_read<T, F>((slot), aoff, boff, (f))
   // One pipeline step u (0..3) of a ring round.  On entry the fragments of the stage in
   // slot u are in registers (set u % 2) and the three following stages are in flight.  The
   // step waits until this wave's loads of the stage in slot u + 1 have landed and its own
@@ -897,40 +928,40 @@ __device__ __attribute__((always_inline)) inline void w_items(
   // (of the next item once the current one runs out).  The MFMAs of the current stage run
   // from registers while the next stage's fragments are read from LDS into the other set;
   // loads and reads are spread between the MFMAs (w_group).  Every issue is
-  // LOADS_PER_STAGE loads per wave, always issued (stages past the end of the work load
+  // WLOADS (2F) loads per wave, always issued (stages past the end of the work load
   // zeros), so "the stage in slot u + 1 has landed" is exactly "at most 2 stages of loads
   // outstanding".  The last step of an item reads nothing: the next item's first stage is
   // read after the epilogue, so that no operand fragments are live while the accumulators
   // are written out.
 #define W_STEP(ctx, st, u, READ_NEXT)                                                       \
   do {                                                                                    \
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LOADS_PER_STAGE));                            \
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * WLOADS));                                     \
     __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                                                \
     SWG_COMPILER_FENCE();                                                                 \
     __builtin_amdgcn_s_barrier();                                                         \
     SWG_COMPILER_FENCE();                                                                 \
-    const WIssue is_ = issue((ctx), (st), ring + (u) * SLOT);                              \
-    w_groups<T, RAGGED, (READ_NEXT)>(std::make_integer_sequence<int, 16>{}, acc,           \
-                                     frags[(u) & 1], frags[((u) + 1) & 1],                \
-                                     ring + (((u) + 1) & 3) * SLOT, aoff, boff, is_, xbase, \
-                                     dbase, lcol);                                        \
+    const WIssue is_ = issue((ctx), (st), ring + (u) * WSLOT);                             \
+    w_groups<T, F, RAGGED, (READ_NEXT)>(std::make_integer_sequence<int, 4 * F>{}, acc,     \
+                                        frags[(u) & 1], frags[((u) + 1) & 1],             \
+                                        ring + (((u) + 1) & 3) * WSLOT, aoff, boff, is_,   \
+                                        xbase, dbase, lcol);                              \
   } while (0)
 
-  f32x16 acc[FP][FQ];
-  FragSet<T> frags[2];
-  WItem cur = w_item(f0, my_items > 0, tiles, tnh, mp, M);
+  f32x16 acc[F][F];
+  FragSet<T, F> frags[2];
+  WItem cur = w_item<F>(f0, my_items > 0, tiles, tnh, mp, M);
   // prologue: the first four stages in flight, the first landed for every wave
   w_issue_all<RAGGED>(issue(cur, 0, ring), xbase, dbase, lcol);
-  w_issue_all<RAGGED>(issue(cur, 1, ring + SLOT), xbase, dbase, lcol);
-  w_issue_all<RAGGED>(issue(cur, 2, ring + 2 * SLOT), xbase, dbase, lcol);
-  w_issue_all<RAGGED>(issue(cur, 3, ring + 3 * SLOT), xbase, dbase, lcol);
-  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * LOADS_PER_STAGE));
+  w_issue_all<RAGGED>(issue(cur, 1, ring + WSLOT), xbase, dbase, lcol);
+  w_issue_all<RAGGED>(issue(cur, 2, ring + 2 * WSLOT), xbase, dbase, lcol);
+  w_issue_all<RAGGED>(issue(cur, 3, ring + 3 * WSLOT), xbase, dbase, lcol);
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * WLOADS));
   SWG_COMPILER_FENCE();
   __builtin_amdgcn_s_barrier();
   SWG_COMPILER_FENCE();
   const int64_t R2 = 2 * N;
   for (int64_t j = 0; j < my_items; ++j) {
-    const WItem nxt = w_item(f0 + (j + 1) * G, j + 1 < my_items, tiles, tnh, mp, M);
+    const WItem nxt = w_item<F>(f0 + (j + 1) * G, j + 1 < my_items, tiles, tnh, mp, M);
     zero_acc(acc);
     W_READ(ring, frags[0]);
     int64_t t = 0;
@@ -945,7 +976,7 @@ __device__ __attribute__((always_inline)) inline void w_items(
     W_STEP(nxt, 2, 2, true);
     W_STEP(nxt, 3, 3, false);   // the next tile's first stage is read after the epilogue
     // epilogue: rows k, columns n (of dg or dfc) straight from the accumulators
-    const int64_t k0 = (int64_t)cur.k0 + wp * 128, n0 = (int64_t)cur.n0 + wq * 128;
+    const int64_t k0 = (int64_t)cur.k0 + wp * WR, n0 = (int64_t)cur.n0 + wq * WR;
     if (ws != nullptr) {
       // fp32 partials in the [K, 2N] layout of split s
       float* dst = ws + (int64_t)cur.s * K * R2 + (cur.hi ? N : 0);
@@ -957,14 +988,16 @@ __device__ __attribute__((always_inline)) inline void w_items(
       T* dw = cur.hi ? dwfc : dwg;
       int ln = lane;
       asm volatile("" : "+v"(ln));   // lane terms formed here, not hoisted (see for_each_pair)
-      const int64_t krows = K - k0 < 128 ? K - k0 : 128;
+      const int64_t krows = K - k0 < WR ? K - k0 : WR;
       const __amdgpu_buffer_rsrc_t r = make_rsrc(dw + k0 * N + n0, clamp_bytes(krows, N * 2));
       const uint32_t row_bytes = (uint32_t)(N * 2);
       const int cols_left = (int)(N - n0);
-      rmw_block_rows<T, 0>(acc, ln, r, row_bytes, cols_left);
-      rmw_block_rows<T, 1>(acc, ln, r, row_bytes, cols_left);
-      rmw_block_rows<T, 2>(acc, ln, r, row_bytes, cols_left);
-      rmw_block_rows<T, 3>(acc, ln, r, row_bytes, cols_left);
+      rmw_block_rows<T, F, 0>(acc, ln, r, row_bytes, cols_left);
+      rmw_block_rows<T, F, 1>(acc, ln, r, row_bytes, cols_left);
+      if constexpr (F == 4) {
+        rmw_block_rows<T, F, 2>(acc, ln, r, row_bytes, cols_left);
+        rmw_block_rows<T, F, 3>(acc, ln, r, row_bytes, cols_left);
+      }
     }
     cur = nxt;
   }
@@ -973,16 +1006,16 @@ __device__ __attribute__((always_inline)) inline void w_items(
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
-template <typename T, bool RAGGED>
+template <typename T, int F, bool RAGGED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void w_stage_kernel(
     const T* __restrict__ x, const T* __restrict__ dg, const T* __restrict__ dfc,
     T* __restrict__ dwg, T* __restrict__ dwfc, float* __restrict__ ws, int64_t M, int64_t K,
     int64_t N, int64_t tnh, int64_t tiles, int64_t split_rows, int64_t nitems) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[4 * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[Tc<F>::W_RING];
   const int64_t G = gridDim.x;
   const WMap mp{split_rows, 0, 0};
-  w_items<T, RAGGED>(ring, x, dg, dfc, dwg, dwfc, ws, M, K, N, tnh, tiles, mp, nitems,
-                     xcd_remap(blockIdx.x, G), G);
+  w_items<T, F, RAGGED>(ring, x, dg, dfc, dwg, dwfc, ws, M, K, N, tnh, tiles, mp, nitems,
+                        xcd_remap(blockIdx.x, G), G);
 }
 
 // ------------------------------------------------------------- fused w + x pass
@@ -995,23 +1028,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // tiles cover the same 64 chunks); the stretch is read from HBM once and found again in
 // the last-level cache.  The w items' fp32 partials per split are summed by
 // w_reduce_kernel in split order, as in the w stage.
-template <typename T, bool RAGGED>
+template <typename T, int F, bool RAGGED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void wx_fused_kernel(
     const T* __restrict__ x, const T* __restrict__ dg, const T* __restrict__ dfc,
     const T* __restrict__ wg, const T* __restrict__ wfc, T* __restrict__ dx,
     T* __restrict__ dwg, T* __restrict__ dwfc, float* __restrict__ ws, int64_t M, int64_t K,
     int64_t N, int64_t nq, int64_t x_ntiles, int64_t gx, int64_t tnh, int64_t w_tiles,
     int64_t chunk_rows, int64_t nsplit, int64_t w_nitems) {
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[X_RING_ELEMS];
-  static_assert(X_RING_ELEMS >= 4 * SLOT, "the w-stage ring must fit the shared array");
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[Tc<F>::RING];
   const int64_t b = blockIdx.x;
   if (b < gx) {
-    x_tiles<T, RAGGED>(ring, dg, dfc, wg, wfc, dx, M, K, N, nq, x_ntiles, xcd_remap(b, gx), gx);
+    x_tiles<T, F, RAGGED>(ring, dg, dfc, wg, wfc, dx, M, K, N, nq, x_ntiles, xcd_remap(b, gx),
+                          gx);
   } else {
     const int64_t gw = (int64_t)gridDim.x - gx;
     const WMap mp{0, chunk_rows, nsplit};
-    w_items<T, RAGGED>(ring, x, dg, dfc, dwg, dwfc, ws, M, K, N, tnh, w_tiles, mp, w_nitems,
-                       xcd_remap(b - gx, gw), gw);
+    w_items<T, F, RAGGED>(ring, x, dg, dfc, dwg, dwfc, ws, M, K, N, tnh, w_tiles, mp, w_nitems,
+                          xcd_remap(b - gx, gw), gw);
   }
 }
 
@@ -1052,15 +1085,6 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, int64_t wor
 // tiles: 256 accumulators, as in the backward GEMMs).  Slot layout: [256 rows of x][32]
 // then [32 k-rows of W_g][128] then [32 k-rows of W_fc][128] (32 KiB).
 constexpr int FN = 128;   // output columns of g (and of fc) per tile
-
-// transposing-read fragment of 16 contraction rows from a [k][RL] tile (see w_frag)
-template <typename T, int RL>
-__device__ inline typename Mfma<T>::frag tr_frag(const uint16_t* p) {
-  const i16x4 lo = tr_read(p);
-  const i16x4 hi = tr_read(p + 4 * RL);
-  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(typename Mfma<T>::frag, v);
-}
 
 struct FTile {   // first row of x / of the outputs, first column of W / of the outputs
   int p0, n0;
@@ -1341,34 +1365,60 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
-template <typename T>
-static hipError_t x_stage_t(const void* dg, const void* dfc, const void* wg, const void* wfc,
-                            void* dx, int64_t M, int64_t K, int64_t N, int cus,
-                            hipStream_t stream) {
-  const int64_t np = ceil_div(M, BP), nq = ceil_div(K, BQ);
-  const int64_t ntiles = np * nq;
-  const int64_t grid = ntiles < cus ? ntiles : cus;
+template <typename T, int F>
+static void x_stage_f(const XPlan& p, const void* dg, const void* dfc, const void* wg,
+                      const void* wfc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
+                      hipStream_t stream) {
+  const int64_t grid = p.tiles < cus ? p.tiles : cus;
   // per-lane column tests unless every double stage is whole: N a multiple of 64 and at
   // least two double stages per half (N = 64 pads the half with a stage past N)
   if (N % XA_BR == 0 && N >= 2 * XA_BR)
-    SWG_LAUNCH((x_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                       static_cast<const T*>(dg), static_cast<const T*>(dfc),
-                       static_cast<const T*>(wg), static_cast<const T*>(wfc),
-                       static_cast<T*>(dx), M, K, N, nq, ntiles);
+    SWG_LAUNCH((x_stage_kernel<T, F, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+               static_cast<const T*>(dg), static_cast<const T*>(dfc),
+               static_cast<const T*>(wg), static_cast<const T*>(wfc), static_cast<T*>(dx), M,
+               K, N, p.nq, p.tiles);
   else
-    SWG_LAUNCH((x_stage_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                       static_cast<const T*>(dg), static_cast<const T*>(dfc),
-                       static_cast<const T*>(wg), static_cast<const T*>(wfc),
-                       static_cast<T*>(dx), M, K, N, nq, ntiles);
+    SWG_LAUNCH((x_stage_kernel<T, F, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
+               static_cast<const T*>(dg), static_cast<const T*>(dfc),
+               static_cast<const T*>(wg), static_cast<const T*>(wfc), static_cast<T*>(dx), M,
+               K, N, p.nq, p.tiles);
+}
+
+template <typename T>
+static hipError_t x_stage_t(const void* dg, const void* dfc, const void* wg, const void* wfc,
+                            void* dx, int64_t M, int64_t K, int64_t N, int force_f, int cus,
+                            hipStream_t stream) {
+  const XPlan p = plan_x(M, K, N, force_f);
+  if (p.f == 4) x_stage_f<T, 4>(p, dg, dfc, wg, wfc, dx, M, K, N, cus, stream);
+  else x_stage_f<T, 2>(p, dg, dfc, wg, wfc, dx, M, K, N, cus, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_x_stage(int dtype, const void* dg, const void* dfc, const void* w_g,
-                          const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
-                          hipStream_t stream) {
-  if (dtype == 0) return x_stage_t<bf16>(dg, dfc, w_g, w_fc, dx, M, K, N, cus, stream);
-  if (dtype == 1) return x_stage_t<fp16>(dg, dfc, w_g, w_fc, dx, M, K, N, cus, stream);
+                          const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N,
+                          int force_f, int cus, hipStream_t stream) {
+  if (dtype == 0) return x_stage_t<bf16>(dg, dfc, w_g, w_fc, dx, M, K, N, force_f, cus, stream);
+  if (dtype == 1) return x_stage_t<fp16>(dg, dfc, w_g, w_fc, dx, M, K, N, force_f, cus, stream);
   return launch_x_stage32(dg, dfc, w_g, w_fc, dx, M, K, N, stream);
+}
+
+template <typename T, int F>
+static void w_stage_f(const WPlan& p, const void* x, const void* dg, const void* dfc,
+                      void* dwg, void* dwfc, int64_t M, int64_t K, int64_t N, float* wsp,
+                      int cus, hipStream_t stream) {
+  const int64_t nitems = p.splits * p.tiles;
+  const int64_t grid = nitems < cus ? nitems : cus;
+  // per-lane column tests only for tiles cut by the right or bottom edge of dW
+  if (K % Tc<F>::P == 0 && N % Tc<F>::P == 0)
+    SWG_LAUNCH((w_stage_kernel<T, F, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
+               static_cast<const T*>(x), static_cast<const T*>(dg), static_cast<const T*>(dfc),
+               static_cast<T*>(dwg), static_cast<T*>(dwfc), wsp, M, K, N, p.tn / 2, p.tiles,
+               p.rows, nitems);
+  else
+    SWG_LAUNCH((w_stage_kernel<T, F, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
+               static_cast<const T*>(x), static_cast<const T*>(dg), static_cast<const T*>(dfc),
+               static_cast<T*>(dwg), static_cast<T*>(dwfc), wsp, M, K, N, p.tn / 2, p.tiles,
+               p.rows, nitems);
 }
 
 template <typename T>
@@ -1376,19 +1426,8 @@ static hipError_t w_stage_t(const WPlan& p, const void* x, const void* dg, const
                             void* dwg, void* dwfc, int64_t M, int64_t K, int64_t N, float* ws,
                             int cus, hipStream_t stream) {
   float* wsp = p.splits > 1 ? ws : nullptr;
-  const int64_t nitems = p.splits * p.tiles;
-  const int64_t grid = nitems < cus ? nitems : cus;
-  // per-lane column tests only for tiles cut by the right or bottom edge of dW
-  if (K % BP == 0 && N % BQ == 0)
-    SWG_LAUNCH((w_stage_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                       static_cast<const T*>(x), static_cast<const T*>(dg),
-                       static_cast<const T*>(dfc), static_cast<T*>(dwg), static_cast<T*>(dwfc),
-                       wsp, M, K, N, p.tn / 2, p.tiles, p.rows, nitems);
-  else
-    SWG_LAUNCH((w_stage_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                       static_cast<const T*>(x), static_cast<const T*>(dg),
-                       static_cast<const T*>(dfc), static_cast<T*>(dwg), static_cast<T*>(dwfc),
-                       wsp, M, K, N, p.tn / 2, p.tiles, p.rows, nitems);
+  if (p.f == 4) w_stage_f<T, 4>(p, x, dg, dfc, dwg, dwfc, M, K, N, wsp, cus, stream);
+  else w_stage_f<T, 2>(p, x, dg, dfc, dwg, dwfc, M, K, N, wsp, cus, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   int64_t blocks = ceil_div(K * 2 * N / 4, 256);
@@ -1420,16 +1459,23 @@ static hipError_t wx_t(const WXPlan& p, const void* x, const void* dg, const voi
   float* wsp = p.splits > 1 ? ws : nullptr;
   const int64_t grid = p.gx + p.gw;
   // the fast (non-ragged) walks need whole x-stage double stages and whole dW tiles
-  const bool whole = N % XA_BR == 0 && N >= 2 * XA_BR && K % BP == 0 && N % BQ == 0;
+  const int64_t edge = tile_edge(p.f);
+  const bool whole = N % XA_BR == 0 && N >= 2 * XA_BR && K % edge == 0 && N % edge == 0;
 #define SWG_WX_ARGS                                                                          \
   static_cast<const T*>(x), static_cast<const T*>(dg), static_cast<const T*>(dfc),          \
       static_cast<const T*>(wg), static_cast<const T*>(wfc), static_cast<T*>(dx),            \
       static_cast<T*>(dwg), static_cast<T*>(dwfc), wsp, M, K, N, p.nq, p.x_tiles, p.gx,      \
       p.tn / 2, p.w_tiles, p.chunk_rows, p.splits, p.w_items
-  if (whole)
-    SWG_LAUNCH((wx_fused_kernel<T, false>), dim3((unsigned)grid), dim3(NT), 0, stream, SWG_WX_ARGS);
-  else
-    SWG_LAUNCH((wx_fused_kernel<T, true>), dim3((unsigned)grid), dim3(NT), 0, stream, SWG_WX_ARGS);
+#define SWG_WX_LAUNCH(F_, R_)                                                                \
+  SWG_LAUNCH((wx_fused_kernel<T, F_, R_>), dim3((unsigned)grid), dim3(NT), 0, stream, SWG_WX_ARGS)
+  if (p.f == 4) {
+    if (whole) SWG_WX_LAUNCH(4, false);
+    else SWG_WX_LAUNCH(4, true);
+  } else {
+    if (whole) SWG_WX_LAUNCH(2, false);
+    else SWG_WX_LAUNCH(2, true);
+  }
+#undef SWG_WX_LAUNCH
 #undef SWG_WX_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;

@@ -71,9 +71,10 @@ hipError_t launch_wx(int dtype, const WXPlan& p, const void* x, const void* dg, 
                      const void* w_g, const void* w_fc, void* dw_g, void* dw_fc, void* dx,
                      int64_t M, int64_t K, int64_t N, float* ws, hipStream_t stream);
 
+// force_f: tile configuration override (4 or 2; 0 = the planner's choice)
 hipError_t launch_x_stage(int dtype, const void* dg, const void* dfc, const void* w_g,
-                          const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
-                          hipStream_t stream);
+                          const void* w_fc, void* dx, int64_t M, int64_t K, int64_t N,
+                          int force_f, int cus, hipStream_t stream);
 
 // fp32 tensors (dtype 2) of the GEMMs; called by launch_x_stage / launch_w_stage / launch_fwd
 hipError_t launch_x_stage32(const void* dg, const void* dfc, const void* w_g, const void* w_fc,

@@ -95,30 +95,84 @@ inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
 }
 
 // ---------------------------------------------------------------- GEMM tiles
-// Both GEMMs use 256 x 256 output tiles and a 64-deep contraction step per LDS stage.
-constexpr int kTileP = 256;     // output rows per workgroup
-constexpr int kTileQ = 256;     // output cols per workgroup
+// Both GEMMs use square output tiles of edge 64 F per workgroup of four waves: F = 4
+// (256 x 256) or F = 2 (128 x 128), and a 32-deep contraction step per LDS stage (the
+// x stage moves two stages per load).
+constexpr int kTileP = 256;     // output rows per workgroup at F = 4
+constexpr int kTileQ = 256;     // output cols per workgroup at F = 4
 constexpr int kTileR = 32;      // contraction depth per LDS stage
 constexpr int64_t kMaxGemmDim = int64_t(1) << 22;  // K, N limit of the GEMM stages
+inline int64_t tile_edge(int f) { return 64 * (int64_t)f; }
+
+// Tile choice.  256 x 256 tiles load half the operand bytes per flop of 128 x 128 tiles
+// and run faster per flop; 128 x 128 tiles win when the large ones leave CUs idle (small
+// batches) or, in the w stage, need many M splits whose fp32 partials cost a round trip
+// through memory.  The planner takes the configuration with the smaller time estimate:
+// rounds of work items over the CUs x pipeline stages per item x the time of one stage
+// at that configuration, plus, for the w stage, the partials' write and read at the
+// streaming rate and the reduce launch.  Stage times from kernel spans on MI355X (bf16,
+// both tile sizes forced, M = 256 .. 220000 at K = 512, N = 1024 and four shapes with K, N
+// up to 4096 and 14336): at 128 x 128 one workgroup per CU is bound by LDS traffic (the
+// DMA writes plus the fragment reads of twice as many bytes per flop), so its stage takes
+// 0.4-0.45 of a 256 x 256 stage for a quarter of the work.
+constexpr int64_t kGemmSlots = 256;        // one persistent workgroup per CU of the MI355X
+constexpr int64_t kXStageNs[2] = {1700, 750};   // x: one 64-deep double stage, F = 4 / F = 2
+constexpr int64_t kWStageNs[2] = {850, 320};    // w: one 32-deep stage, F = 4 / F = 2
+constexpr int64_t kReduceLaunchNs = 2000;       // w_reduce launch and ramp
+constexpr int64_t kStreamBytesPerNs = 5000;     // partials' round trip, ~5 TB/s
+inline int64_t stage_ns(const int64_t (&t)[2], int f) { return f == 4 ? t[0] : t[1]; }
+
+// x stage: output [M, K] in tiles of edge 64 F; every tile runs nds double stages.
+struct XPlan {
+  int f;
+  int64_t nq, tiles;       // column tiles per row block, tiles
+};
+
+inline int64_t x_double_stages(int64_t N) {
+  const int64_t sd = ceil_div(N, 2 * kTileR);
+  return 2 * (sd < 2 ? 2 : sd);
+}
+
+inline XPlan plan_x_f(int64_t M, int64_t K, int f) {
+  XPlan p{};
+  p.f = f;
+  p.nq = ceil_div(K, tile_edge(f));
+  p.tiles = ceil_div(M, tile_edge(f)) * p.nq;
+  return p;
+}
+
+inline int64_t x_time_ns(const XPlan& p, int64_t N, int64_t slots) {
+  return ceil_div(p.tiles, slots) * x_double_stages(N) * stage_ns(kXStageNs, p.f);
+}
+
+// force_f: 4 or 2 overrides the estimate (0: the planner's choice); likewise below.
+inline XPlan plan_x(int64_t M, int64_t K, int64_t N, int force_f = 0) {
+  if (force_f == 4 || force_f == 2) return plan_x_f(M, K, force_f);
+  const XPlan big = plan_x_f(M, K, 4), small = plan_x_f(M, K, 2);
+  return x_time_ns(small, N, kGemmSlots) < x_time_ns(big, N, kGemmSlots) ? small : big;
+}
 
 // w stage: output [K, 2N]; when it has too few tiles to fill the chip the batch
 // dimension M is split into S ranges whose fp32 partials are summed in order.
 struct WPlan {
+  int f;                   // tile configuration
   int64_t tk, tn, tiles;   // tile grid over [K, 2N]: tn / 2 column tiles in dg, tn / 2 in dfc
   int64_t splits;          // S
   int64_t rows;            // rows of M per split (multiple of kTileR)
   size_t ws_bytes;         // S > 1: S * K * 2N * sizeof(float)
 };
 
-constexpr int64_t kWTargetBlocks = 256;
+constexpr int64_t kWTargetBlocks = kGemmSlots;
 constexpr int64_t kWMinRowsPerSplit = 512;
 
-inline WPlan plan_w(int64_t M, int64_t K, int64_t N) {
+inline WPlan plan_w_f(int64_t M, int64_t K, int64_t N, int f) {
   WPlan p{};
-  p.tk = ceil_div(K, kTileP);
-  p.tn = 2 * ceil_div(N, kTileQ);
+  p.f = f;
+  p.tk = ceil_div(K, tile_edge(f));
+  p.tn = 2 * ceil_div(N, tile_edge(f));
   p.tiles = p.tk * p.tn;
-  int64_t s = p.tiles > 0 ? ceil_div(kWTargetBlocks, p.tiles) : 1;
+  // splits that keep tiles x S within one round of workgroups
+  int64_t s = p.tiles > 0 ? kWTargetBlocks / p.tiles : 1;
   const int64_t smax = M / kWMinRowsPerSplit;
   if (s > smax) s = smax;
   if (s < 1) s = 1;
@@ -132,13 +186,28 @@ inline WPlan plan_w(int64_t M, int64_t K, int64_t N) {
   return p;
 }
 
+inline int64_t w_time_ns(const WPlan& p) {
+  const int64_t nst = 4 * ceil_div(p.rows, 4 * kTileR);   // whole ring rounds per item
+  int64_t t = ceil_div(p.splits * p.tiles, kWTargetBlocks) * nst * stage_ns(kWStageNs, p.f);
+  if (p.splits > 1) t += kReduceLaunchNs + 2 * (int64_t)p.ws_bytes / kStreamBytesPerNs;
+  return t;
+}
+
+inline WPlan plan_w(int64_t M, int64_t K, int64_t N, int force_f = 0) {
+  if (force_f == 4 || force_f == 2) return plan_w_f(M, K, N, force_f);
+  const WPlan big = plan_w_f(M, K, N, 4), small = plan_w_f(M, K, N, 2);
+  return w_time_ns(small) < w_time_ns(big) ? small : big;
+}
+
 // fused w + x pass: the grid is split between x-stage tiles (gx workgroups) and w-stage
 // items (gw workgroups).  Both GEMMs have the same flop count, so half of the workgroups
 // go to each; the w items are the dW tiles times S splits over 256-row chunks taken
 // round-robin, S chosen so the w half of the grid is filled (and at least 512 rows per
 // split, as in the w stage).  With 128 + 128 workgroups both halves advance through the
-// rows of [dg | dfc] at the same rate.
+// rows of [dg | dfc] at the same rate.  Both halves use 128 x 128 tiles when the x stage
+// has fewer 256 x 256 tiles than its half of the grid.
 struct WXPlan {
+  int f;                           // tile configuration of both halves
   int64_t nq, x_tiles, gx;         // x stage: column tiles per row block, tiles, workgroups
   int64_t tn, w_tiles, splits;     // w stage: tile grid, tiles, S
   int64_t w_items, gw;             // items (tiles x S), workgroups
@@ -149,14 +218,17 @@ struct WXPlan {
 constexpr int64_t kWXChunkRows = 256;
 constexpr int64_t kWXWorkgroups = 256;
 
-inline WXPlan plan_wx(int64_t M, int64_t K, int64_t N) {
+inline WXPlan plan_wx(int64_t M, int64_t K, int64_t N, int force_f = 0) {
   WXPlan p{};
-  p.nq = ceil_div(K, kTileQ);
-  p.x_tiles = ceil_div(M, kTileP) * p.nq;
+  p.f = ceil_div(M, tile_edge(4)) * ceil_div(K, tile_edge(4)) < kWXWorkgroups / 2 ? 2 : 4;
+  if (force_f == 4 || force_f == 2) p.f = force_f;
+  const int64_t edge = tile_edge(p.f);
+  p.nq = ceil_div(K, edge);
+  p.x_tiles = ceil_div(M, edge) * p.nq;
   p.gx = p.x_tiles < kWXWorkgroups / 2 ? p.x_tiles : kWXWorkgroups / 2;
   if (p.gx < 1) p.gx = 1;
-  p.tn = 2 * ceil_div(N, kTileQ);
-  p.w_tiles = ceil_div(K, kTileP) * p.tn;
+  p.tn = 2 * ceil_div(N, edge);
+  p.w_tiles = ceil_div(K, edge) * p.tn;
   const int64_t target = kWXWorkgroups - p.gx;
   int64_t s = p.w_tiles > 0 ? target / p.w_tiles : 1;
   const int64_t smax = M / kWMinRowsPerSplit;

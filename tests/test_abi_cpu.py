@@ -303,6 +303,40 @@ def test_overlapping_outputs_are_rejected(lib):
         assert lib.swiglu_fwd(*fa(**{k: alias})) == INVALID, (k, alias)
 
 
+def test_gemm_tile_query_and_override(lib):
+    """The planner's tile choice (host arithmetic, no device needed) and the thread-local
+    override that the GPU tests use to run every GEMM shape at both tile sizes."""
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    t = swg.swiglu_bwd_gemm_tile
+    # the large-batch and LLM-sized FFNs keep 256 x 256 tiles in the x stage; the tiny and
+    # ragged batches, which have too few of them for 256 CUs, take 128 x 128
+    assert t("x", 220000, 512, 1024, bf) == 256 and t("x", 16384, 4096, 14336, bf) == 256
+    assert t("x", 8191, 512, 1024, bf) == 128 and t("x", 256, 64, 128, bf) == 128
+    assert t("w", 16384, 4096, 14336, bf) == 256 and t("w", 8191, 512, 1024, bf) == 128
+    assert t("wx", 220000, 512, 1024, bf) == 256 and t("wx", 8191, 512, 1024, bf) == 128
+    for st in ("w", "x", "wx"):
+        assert t(st, 0, 64, 128, bf) == 0 and t(st, 256, 64, 128, f32) == 0
+        assert t(st, 256, 60, 128, bf) == 0          # K not a multiple of 8
+    assert lib.swiglu_bwd_gemm_tile(7, 256, 64, 128, BF16) == 0
+    for bad in (64, -1, 512, 1):
+        assert lib.swg_set_gemm_tile(bad) == INVALID
+    try:
+        for edge in (128, 256):
+            assert lib.swg_set_gemm_tile(edge) == OK
+            for st in ("w", "x", "wx"):
+                assert t(st, 220000, 512, 1024, bf) == edge
+                assert t(st, 8191, 512, 1024, bf) == edge
+            # w stage at M = 8191: the M splits fill one round of 256 workgroups with the
+            # tiles of that size, at least 512 rows each
+            tiles = (512 // edge) * 2 * (1024 // edge)
+            splits = swg.swiglu_bwd_w_workspace_size(8191, 512, 1024, bf) // (512 * 2048 * 4)
+            assert splits == min(256 // tiles, 8191 // 512)
+    finally:
+        assert lib.swg_set_gemm_tile(0) == OK
+    assert t("x", 8191, 512, 1024, bf) == 128 and t("x", 220000, 512, 1024, bf) == 256
+
+
 def test_workspace_queries():
     import torch
     b = swg.swiglu_bwd_b_workspace_size

@@ -62,7 +62,7 @@ def _fused_case(inp, dt, dw0=None):
 
 @pytest.mark.parametrize("wl", ["tiny", "ragged"])
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
-def test_fused_workloads(wl, dt):
+def test_fused_workloads(wl, dt, tile):
     _fused_case(swiglu_inputs(wl, dtype=dt), dt)
 
 
@@ -77,12 +77,12 @@ def test_fused_accumulates_into_nonzero_dw():
                                    (257, 520, 8), (700, 256, 128), (513, 1032, 72),
                                    (2000, 64, 2048), (4099, 256, 256), (20000, 512, 64)])
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
-def test_fused_odd_shapes(M, K, N, dt):
+def test_fused_odd_shapes(M, K, N, dt, tile):
     _fused_case(swiglu_inputs(SwiGLUShape("fodd", 23, M, K, N), dtype=dt), dt)
 
 
 @pytest.mark.parametrize("seed", range(8))
-def test_fused_random_shapes(seed):
+def test_fused_random_shapes(seed, tile):
     rng = np.random.default_rng(3000 + seed)
     M = int(rng.integers(1, 12000))
     K = int(rng.integers(1, 1100 // 8 + 1)) * 8

@@ -112,13 +112,13 @@ def test_b_stage_unaligned_rows_use_scalar_path():
 
 @pytest.mark.parametrize("wl", ["tiny", "ragged"])
 @pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
-def test_w_stage_workloads(wl, dt):
+def test_w_stage_workloads(wl, dt, tile):
     inp = swiglu_inputs(wl, dtype=dt)
     dg, dfc = _oracle_dg(inp, dt)
     _w_case(inp["x"], dg, dfc, dt)
 
 
-def test_w_stage_accumulates_into_nonzero_dw():
+def test_w_stage_accumulates_into_nonzero_dw(tile):
     inp = swiglu_inputs("ragged", dtype="bf16")
     dg, dfc = _oracle_dg(inp, "bf16")
     K, N = inp["w_g"].shape
@@ -128,7 +128,7 @@ def test_w_stage_accumulates_into_nonzero_dw():
 
 @pytest.mark.parametrize("wl", ["tiny", "ragged"])
 @pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
-def test_x_stage_workloads(wl, dt):
+def test_x_stage_workloads(wl, dt, tile):
     inp = swiglu_inputs(wl, dtype=dt)
     dg, dfc = _oracle_dg(inp, dt)
     _x_case(dg, dfc, inp["w_g"], inp["w_fc"], dt)
@@ -138,7 +138,7 @@ def test_x_stage_workloads(wl, dt):
                                    (257, 520, 8), (700, 256, 128), (513, 1032, 72),
                                    (2000, 64, 2048), (300, 200, 64), (129, 96, 192)])
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])
-def test_gemm_stages_odd_shapes(M, K, N, dt):
+def test_gemm_stages_odd_shapes(M, K, N, dt, tile):
     inp = swiglu_inputs(SwiGLUShape("odd", 13, M, K, N), dtype=dt)
     dg, dfc = _oracle_dg(inp, dt)
     _w_case(inp["x"], dg, dfc, dt)
@@ -155,6 +155,29 @@ def test_gemm_stages_fp32_odd_shapes(M, K, N):
     _x_case(dg, dfc, inp["w_g"], inp["w_fc"], "fp32")
 
 
+@pytest.mark.parametrize("M,K,N", [(8191, 512, 1024), (300, 264, 264), (2000, 64, 2048),
+                                   (513, 1032, 72), (20000, 520, 1000)])
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_x_stage_bits_do_not_depend_on_tile(M, K, N, dt):
+    """Every dx element sees the same matrix-core operations in the same contraction order
+    at either tile size, so the two configurations give the same bits."""
+    dev = device()
+    inp = swiglu_inputs(SwiGLUShape("xtile", 15, M, K, N), dtype=dt)
+    d = {k: inp[k].to(dev) for k in ("dy", "w_g", "w_fc")}
+    out = {}
+    for edge in (128, 256):
+        note(f"x stage tile {edge} M={M} K={K} N={N} {dt}")
+        swg.swg_set_gemm_tile(edge)
+        try:
+            dx = torch.empty(M, K, dtype=DTYPES[dt], device=dev)
+            swg.swiglu_bwd_x(d["dy"], d["dy"], d["w_g"], d["w_fc"], dx)
+            torch.cuda.synchronize()
+            out[edge] = dx.cpu()
+        finally:
+            swg.swg_set_gemm_tile(0)
+    assert torch.equal(out[128].view(torch.int16), out[256].view(torch.int16))
+
+
 def _random_shape(seed, vec):
     """A seeded shape with K, N multiples of `vec` (the 16-byte row rule), sizes spread
     over several tiles and partial tiles on every side."""
@@ -166,7 +189,7 @@ def _random_shape(seed, vec):
 
 
 @pytest.mark.parametrize("seed", range(12))
-def test_gemm_stages_random_shapes(seed):
+def test_gemm_stages_random_shapes(seed, tile):
     """Seeded random shapes (bf16 and fp16 alternately): w and x against the oracle."""
     M, K, N = _random_shape(seed, 8)
     dt = "bf16" if seed % 2 == 0 else "fp16"
