@@ -176,11 +176,24 @@ def time_fused(swg, d, dg, dfc, M, K, N, warmup, steps):
                     "inputs; compare with stages w + x; not part of the step"}
 
 
+class Evictor:
+    """Evicts the 256 MB last-level cache before a cold timed call by reading a 1 GiB
+    buffer (a read-only pass: the timed call then finds its inputs in HBM and no dirty
+    lines of an unrelated kernel left to write back)."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.buf.sum()
+
+
 def time_swish_context(swg, steps):
     """The Swish gradient on the one workload the pages time: an fp16 [32, 64, 56, 56]
     activation with beta = 1 (Ascend C custom-operator page, performance table).  Each
-    call is preceded by a 1 GiB write, so its inputs come from HBM and not from the
-    256 MB last-level cache; each call is timed by its kernel span.  Reported beside
+    call is preceded by a 1 GiB read (Evictor), so its inputs come from HBM and not from
+    the 256 MB last-level cache; each call is timed by its kernel span.  Reported beside
     the step, not part of `value`."""
     import torch
     from workloads.gen import SWISH_CONTEXT, swish_inputs
@@ -192,11 +205,11 @@ def time_swish_context(swg, steps):
     inp = {k: v.reshape(c["shape"]).to(dev) for k, v in
            swish_inputs(c["dtype"], L=L, seed=c["seed"]).items()}
     out = torch.empty_like(inp["grad"])
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    evict = Evictor(dev)
     timer = SpanTimer(swg, steps + 3)
     times = []
     for i in range(steps + 3):
-        flush.fill_(i & 0xFF)
+        evict()
         timer.arm(i)
         swg.swish_grad(inp["grad"], inp["x"], grad_x=out, beta=c["beta"])
         torch.cuda.synchronize()
@@ -209,23 +222,24 @@ def time_swish_context(swg, steps):
             "median_us": round(t * 1e6, 2), "min_us": round(times[0] * 1e6, 2),
             "GB/s": round(nbytes / t / 1e9, 1), "frac": round(nbytes / HBM_PEAK / t, 4),
             "pages_us": {"ascend_c_kernel": 280, "autodiff": 420},
-            "note": "median kernel span of one call after a 1 GiB cache-evicting write; "
+            "note": "median kernel span of one call after a 1 GiB cache-evicting read; "
                     "the pages' times are Ascend 910B, context only"}
 
 
 def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
     """The b, w and x stages and the fused w + x pass at the other SwiGLU workloads (same
     seeded recipe), each
-    stage call preceded by a 1 GiB write that evicts the 256 MB last-level cache (the
-    tiny and ragged working sets would otherwise stay in it) and timed by its kernel span,
-    median over `steps` calls.  Reported beside the step (the tiny and ragged
+    stage call preceded by a 1 GiB read that evicts the 256 MB last-level cache (the
+    tiny and ragged working sets would otherwise stay in it; a read leaves no dirty lines
+    for the timed call to write back) and timed by its kernel span, median over `steps`
+    calls.  Reported beside the step (the tiny and ragged
     shapes are launch- and latency-bound; the LLM-sized FFN is matrix-core bound); not
     part of `value`."""
     import torch
     from workloads.gen import SWIGLU_WORKLOADS, swiglu_inputs
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    evict = Evictor(dev)
     res = {}
     for name in names:
         shape = SWIGLU_WORKLOADS[name]
@@ -257,7 +271,7 @@ def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
         timer = SpanTimer(swg, steps * len(calls))
         for it in range(steps):
             for i, f in enumerate(calls.values()):
-                flush.fill_((it + i) & 0xFF)
+                evict()
                 timer.arm(it * len(calls) + i)
                 f()
         torch.cuda.synchronize()
