@@ -139,7 +139,8 @@ swg_status swiglu_bwd_x(const void* dg, const void* dfc, const void* w_g, const 
  * swiglu_bwd_wx (stage 2) uses for a bf16 or fp16 problem of this shape: 256, or 128 where
  * 256 x 256 tiles would leave CUs of the MI355X idle (small M, small outputs) or, in the w
  * stage, need many fp32 M-split partials.  Host-only arithmetic: the planner the calls
- * themselves use, independent of the device.  Results do not depend on the tile size
+ * themselves use, independent of the device.  Where swiglu_bwd_wx runs the two stages
+ * as separate launches, stage 2 reports the x stage's tile.  Results do not depend on the tile size
  * beyond rounding order.  0 for fp32 (its own kernels), empty or unsupported shapes and an
  * unknown stage.
  */
@@ -166,7 +167,10 @@ swg_status swg_set_gemm_tile(int edge);
  * that both halves read the same rows at about the same time and [dg | dfc] crosses HBM
  * about once (the separate calls read it twice).  dx is bit-identical to swiglu_bwd_x;
  * dW groups its fp32 partial sums by chunk and may differ from swiglu_bwd_w in the last
- * bit.  dtype bf16 or fp16 (fp32: SWG_ERR_UNSUPPORTED); the shape and alignment rules of
+ * bit.  Shapes whose dW grid needs no M split and where each stage alone fills the GPU
+ * (e.g. M = 16384, K = 4096, N = 14336) gain nothing from sharing rows: there the call runs
+ * swiglu_bwd_w and then swiglu_bwd_x (two launches on the stream, the same bits as those
+ * calls).  dtype bf16 or fp16 (fp32: SWG_ERR_UNSUPPORTED); the shape and alignment rules of
  * swiglu_bwd_w and swiglu_bwd_x; dx, dw_g, dw_fc and the workspace may not overlap each
  * other or an input (SWG_ERR_INVALID).  `workspace`: swiglu_bwd_wx_workspace_size(M, K, N,
  * dtype) bytes (S * K * 2N fp32 partials; 0 when S = 1).  N = 0 writes dx = 0 (the

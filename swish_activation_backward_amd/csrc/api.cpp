@@ -422,7 +422,10 @@ int swiglu_bwd_gemm_tile(int stage, int64_t M, int64_t K, int64_t N, swg_dtype d
   int f = 0;
   if (stage == 0) f = plan_w(M, K, N, g_tile_f).f;
   else if (stage == 1) f = plan_x(M, K, N, g_tile_f).f;
-  else if (stage == 2) f = plan_wx(M, K, N, g_tile_f).f;
+  else if (stage == 2) {
+    const WXPlan p = plan_wx(M, K, N, g_tile_f);
+    f = p.separate ? plan_x(M, K, N, g_tile_f).f : p.f;
+  }
   return (int)tile_edge(f);
 }
 
@@ -461,6 +464,14 @@ swg_status swiglu_bwd_wx(const void* x, const void* dg, const void* dfc, const v
                          {workspace, (int64_t)p.ws_bytes}};
     const Span ins[] = {{x, span_bytes(M, K, es)}, {dg, d}, {dfc, d}, {w_g, w}, {w_fc, w}};
     if (!outputs_disjoint(outs, ins)) return SWG_ERR_INVALID;
+  }
+  if (p.separate) {   // no M split to share rows: the two stages, one launch each
+    const hipError_t e = launch_w_stage(dtype, plan_w(M, K, N, g_tile_f), x, dg, dfc, dw_g,
+                                        dw_fc, M, K, N, static_cast<float*>(workspace),
+                                        gemm_grid_cap(), as_stream(stream));
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_x_stage(dtype, dg, dfc, w_g, w_fc, dx, M, K, N, g_tile_f,
+                                     gemm_grid_cap(), as_stream(stream)));
   }
   return hip_status(launch_wx(dtype, p, x, dg, dfc, w_g, w_fc, dw_g, dw_fc, dx, M, K, N,
                               static_cast<float*>(workspace), as_stream(stream)));

@@ -337,6 +337,23 @@ def test_gemm_tile_query_and_override(lib):
     assert t("x", 8191, 512, 1024, bf) == 128 and t("x", 220000, 512, 1024, bf) == 256
 
 
+def test_fused_plan_runs_large_unsplit_shapes_as_two_stages():
+    """Where the dW grid needs no M split and each stage fills the GPU alone, swiglu_bwd_wx
+    runs the w stage and then the x stage: its workspace is the w stage's, and the tile it
+    reports is the x stage's."""
+    import torch
+    bf = torch.bfloat16
+    wx, w = swg.swiglu_bwd_wx_workspace_size, swg.swiglu_bwd_w_workspace_size
+    t = swg.swiglu_bwd_gemm_tile
+    for (M, K, N) in ((16384, 4096, 14336), (4096, 4096, 14336), (4096, 4096, 4096)):
+        assert wx(M, K, N, bf) == w(M, K, N, bf) == 0
+        assert t("wx", M, K, N, bf) == t("x", M, K, N, bf)
+    # fused where the M split shares rows (large batch) or one stage alone under-fills
+    per_split = 512 * 2048 * 4
+    assert wx(220000, 512, 1024, bf) == 8 * per_split      # 8 splits x 16 dW tiles
+    assert wx(2048, 4096, 4096, bf) == 0 and t("wx", 2048, 4096, 4096, bf) == 256
+
+
 def test_workspace_queries():
     import torch
     b = swg.swiglu_bwd_b_workspace_size

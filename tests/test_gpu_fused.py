@@ -91,6 +91,40 @@ def test_fused_random_shapes(seed, tile):
     _fused_case(swiglu_inputs(SwiGLUShape("frand", 80 + seed, M, K, N), dtype=dt), dt)
 
 
+def test_fused_large_unsplit_shape_runs_the_two_stages():
+    """M = 4096, K = 4096, N = 4096: no M split and both stages fill the GPU, so the call
+    runs swiglu_bwd_w then swiglu_bwd_x; every output is bit-identical to those calls."""
+    dev = device()
+    M, K, N = 4096, 4096, 4096
+    bf = torch.bfloat16
+    g = torch.Generator().manual_seed(31)
+    r = lambda *s, sc: (torch.randn(*s, generator=g) * sc).to(bf).to(dev)
+    x, dg, dfc = r(M, K, sc=M ** -0.5), r(M, N, sc=1e-2), r(M, N, sc=1e-2)
+    w_g, w_fc = r(K, N, sc=K ** -0.5), r(K, N, sc=K ** -0.5)
+    dw0 = r(K, N, sc=1e-3)
+    note(f"fused w+x as two stages M={M} K={K} N={N}")
+    fdw_g, fdw_fc, fdx = dw0.clone(), (2 * dw0).clone(), torch.empty(M, K, dtype=bf, device=dev)
+    swg.swiglu_bwd_wx(x, dg, dfc, w_g, w_fc, fdw_g, fdw_fc, fdx)
+    sdw_g, sdw_fc, sdx = dw0.clone(), (2 * dw0).clone(), torch.empty(M, K, dtype=bf, device=dev)
+    swg.swiglu_bwd_w(x, dg, dfc, sdw_g, sdw_fc)
+    swg.swiglu_bwd_x(dg, dfc, w_g, w_fc, sdx)
+    torch.cuda.synchronize()
+    for name, a, b in (("dw_g", fdw_g, sdw_g), ("dw_fc", fdw_fc, sdw_fc), ("dx", fdx, sdx)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+    # and against the oracle on sampled rows / columns
+    cols = np.random.default_rng(5).choice(N, 64, replace=False)
+    rows = np.random.default_rng(6).choice(M, 64, replace=False)
+    xc, dgc, dfcc = x.cpu(), dg.cpu(), dfc.cpu()
+    rg, rf, ag, af = oracle_w_chunked(xc, dgc, dfcc, cols=cols)
+    i64 = to64(dw0.cpu()[:, cols])
+    compare("dw_g cols", fdw_g.cpu()[:, cols], rg + i64, "bf16",
+            model_abs=sum_abs_model(ag + np.abs(i64)))
+    compare("dw_fc cols", fdw_fc.cpu()[:, cols], rf + 2 * i64, "bf16",
+            model_abs=sum_abs_model(af + 2 * np.abs(i64)))
+    ref, a = oracle_x_rows(dgc, dfcc, w_g.cpu(), w_fc.cpu(), rows)
+    compare("dx rows", fdx.cpu()[rows], ref, "bf16", model_abs=sum_abs_model(a))
+
+
 def test_fused_empty_contraction_and_fp32():
     dev = device()
     M, K = 33, 16
