@@ -93,6 +93,9 @@ template <int F> struct Tc {
   static constexpr int W_RING = 4 * WSLOT;
   static constexpr int RPL = 1024 / (2 * P);             // w-stage rows per 1 KiB load
   static constexpr int RING = X_RING > W_RING ? X_RING : W_RING;
+  // x-stage workgroups per CU: at F = 2 the ring (80 KiB) and the registers fit twice, and
+  // a second wave per SIMD raises the LDS read rate the 128 x 128 tile is bound by
+  static constexpr int XOCC = F == 4 ? 1 : 2;
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
@@ -726,7 +729,7 @@ __device__ __attribute__((always_inline)) inline void x_tiles(
 }
 
 template <typename T, int F, bool RAGGED>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void x_stage_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Tc<F>::XOCC, Tc<F>::XOCC))) void x_stage_kernel(
     const T* __restrict__ dg, const T* __restrict__ dfc, const T* __restrict__ wg,
     const T* __restrict__ wfc, T* __restrict__ dx, int64_t M, int64_t K, int64_t N, int64_t nq,
     int64_t ntiles) {
@@ -1369,7 +1372,8 @@ template <typename T, int F>
 static void x_stage_f(const XPlan& p, const void* dg, const void* dfc, const void* wg,
                       const void* wfc, void* dx, int64_t M, int64_t K, int64_t N, int cus,
                       hipStream_t stream) {
-  const int64_t grid = p.tiles < cus ? p.tiles : cus;
+  const int64_t slots = (int64_t)cus * Tc<F>::XOCC;
+  const int64_t grid = p.tiles < slots ? p.tiles : slots;
   // per-lane column tests unless every double stage is whole: N a multiple of 64 and at
   // least two double stages per half (N = 64 pads the half with a stage past N)
   if (N % XA_BR == 0 && N >= 2 * XA_BR)

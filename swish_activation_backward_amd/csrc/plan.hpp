@@ -114,9 +114,12 @@ inline int64_t tile_edge(int f) { return 64 * (int64_t)f; }
 // both tile sizes forced, M = 256 .. 220000 at K = 512, N = 1024 and four shapes with K, N
 // up to 4096 and 14336): at 128 x 128 one workgroup per CU is bound by LDS traffic (the
 // DMA writes plus the fragment reads of twice as many bytes per flop), so its stage takes
-// 0.4-0.45 of a 256 x 256 stage for a quarter of the work.
+// 0.4-0.45 of a 256 x 256 stage for a quarter of the work.  The x stage at 128 x 128 runs
+// two workgroups per CU when it has more tiles than CUs: a double stage then takes 1.15 us
+// per workgroup (two progress at once), against 0.75 us for a workgroup alone.
 constexpr int64_t kGemmSlots = 256;        // one persistent workgroup per CU of the MI355X
 constexpr int64_t kXStageNs[2] = {1700, 750};   // x: one 64-deep double stage, F = 4 / F = 2
+constexpr int64_t kXStageNsShared = 1150;       // x, F = 2, two workgroups per CU
 constexpr int64_t kWStageNs[2] = {850, 320};    // w: one 32-deep stage, F = 4 / F = 2
 constexpr int64_t kReduceLaunchNs = 2000;       // w_reduce launch and ramp
 constexpr int64_t kStreamBytesPerNs = 5000;     // partials' round trip, ~5 TB/s
@@ -142,7 +145,10 @@ inline XPlan plan_x_f(int64_t M, int64_t K, int f) {
 }
 
 inline int64_t x_time_ns(const XPlan& p, int64_t N, int64_t slots) {
-  return ceil_div(p.tiles, slots) * x_double_stages(N) * stage_ns(kXStageNs, p.f);
+  const int64_t nds = x_double_stages(N);
+  if (p.f == 4) return ceil_div(p.tiles, slots) * nds * kXStageNs[0];
+  if (p.tiles <= slots) return nds * kXStageNs[1];   // one workgroup per CU
+  return ceil_div(p.tiles, 2 * slots) * nds * kXStageNsShared;
 }
 
 // force_f: 4 or 2 overrides the estimate (0: the planner's choice); likewise below.
