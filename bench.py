@@ -183,7 +183,9 @@ class Evictor:
 
     def __init__(self, dev):
         import torch
-        self.buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        # float32: torch sums it in place (an int32 sum would first cast to int64, a
+        # 2 GiB write)
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
     def __call__(self):
         self.buf.sum()
