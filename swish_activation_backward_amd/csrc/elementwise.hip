@@ -302,10 +302,14 @@ static hipError_t b_stage_t(const BPlan& p, const void* dy, const void* g, const
   const T* a = static_cast<const T*>(dy);
   const T* b = static_cast<const T*>(g);
   const T* c = static_cast<const T*>(fc);
-  if (p.vec > 1) {
+  if (p.vec > 1 && p.rif == kBRowsInFlight) {
     SWG_LAUNCH((b_stage_kernel<T, true, kBRowsInFlight>), grid, dim3(256), 0, stream, a, b, c,
                        static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.unit_rows,
                        p.nunits, txlog2);
+  } else if (p.vec > 1) {
+    SWG_LAUNCH((b_stage_kernel<T, true, kBSmallRows>), grid, dim3(256), 0, stream, a, b, c,
+               static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.unit_rows,
+               p.nunits, txlog2);
   } else {
     SWG_LAUNCH((b_stage_kernel<T, false, 1>), grid, dim3(256), 0, stream, a, b, c,
                        static_cast<T*>(dg), static_cast<T*>(dfc), part, M, N, p.cv, p.unit_rows,

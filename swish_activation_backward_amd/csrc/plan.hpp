@@ -27,6 +27,7 @@ inline int vec_of(int dtype) { return 16 / elem_size(dtype); }
 // are not a power of two (balanced to whole rounds) ran slower.
 struct BPlan {
   int vec;             // elements per 16-byte access (1 when the scalar path is used)
+  int rif;             // rows whose loads a lane issues before computing (vector path)
   int tx, ty;          // thread layout inside the 256-thread workgroup
   int64_t cv;          // vector columns per row = N / vec
   int64_t nstrips;     // ceil(cv / tx)
@@ -53,6 +54,14 @@ constexpr int64_t kBSlots = 256;
 constexpr size_t kBScratchBytes = size_t(16) << 20;
 constexpr int64_t kBMinBlocks = 1024;
 constexpr int kBRowsInFlight = 8;        // rows whose loads a lane issues before computing
+// Small batches (at most kBSmallBlocks workgroups with kBRowsInFlight rows per lane): the
+// vector kernel holds 300 registers, so one workgroup per CU runs its single pass of
+// loads, then its arithmetic, with nothing to overlap them.  There the plan takes
+// kBSmallRows rows in flight (a kernel several workgroups of which share a CU), units of
+// one pass and one walker per unit (at most kBSmallMaxBlocks workgroups).
+constexpr int kBSmallRows = 4;
+constexpr int64_t kBSmallBlocks = 4096;
+constexpr int64_t kBSmallMaxBlocks = 4096;
 
 inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
   BPlan p{};
@@ -64,10 +73,17 @@ inline BPlan plan_b(int64_t M, int64_t N, int dtype, bool vector_path) {
   while (tx_ref < kBMaxTx && tx_ref < cv_ref) tx_ref <<= 1;
   const int64_t strips_ref = ceil_div(cv_ref, tx_ref);
   const int64_t pass_rows = (int64_t)kBRowsInFlight * (kBThreads / tx_ref);
+  p.rif = kBRowsInFlight;
   p.unit_rows = pass_rows > kBMinUnitRows ? pass_rows : kBMinUnitRows;
   p.nunits = M > 0 ? ceil_div(M, p.unit_rows) : 0;
   int64_t nwalk = 1;
-  if (p.nunits > 0) {
+  if (p.nunits > 0 && strips_ref * p.nunits <= kBSmallBlocks) {
+    p.rif = kBSmallRows;
+    p.unit_rows = (int64_t)kBSmallRows * (kBThreads / tx_ref);
+    p.nunits = ceil_div(M, p.unit_rows);
+    const int64_t cap = kBSmallMaxBlocks / strips_ref;
+    nwalk = p.nunits < cap ? p.nunits : (cap > 0 ? cap : 1);
+  } else if (p.nunits > 0) {
     int64_t w0 = 1;   // smallest power of two reaching kBMinBlocks workgroups
     while (strips_ref * w0 < kBMinBlocks) w0 *= 2;
     int64_t best_cost = -1;

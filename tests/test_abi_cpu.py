@@ -366,26 +366,32 @@ def test_workspace_queries():
         nb = b(M, N, torch.bfloat16)
         assert nb % (2 * N * 4) == 0 and 0 < nb // (2 * N * 4) <= max(M, 1)
         assert nb // (2 * N * 4) <= 4096
-    # b plan: strips of at most 32 16-byte vector columns, units of whole 8-row passes, and
+    # b plan: strips of at most 32 16-byte vector columns; units of whole 8-row passes and
     # a power-of-two walker count per strip (or every unit) chosen for whole rounds of 256
-    # resident workgroups; pinned at the workload shapes
+    # resident workgroups, except for small batches (at most 4096 workgroups that way),
+    # which take units of one 4-row pass and one walker per unit; pinned at the workload
+    # shapes
     for (M, N, dt, strips, walkers) in ((220000, 1024, torch.bfloat16, 4, 256),
                                         (16384, 14336, torch.bfloat16, 56, 32),
                                         (16384, 14336, torch.float32, 112, 16),
                                         (220000, 1024, torch.float32, 8, 128),
-                                        (8191, 1024, torch.float16, 4, 128),
-                                        (256, 128, torch.bfloat16, 1, 2),
-                                        (4097, 24, torch.bfloat16, 1, 9)):
+                                        (8191, 1024, torch.float16, 4, 256),
+                                        (256, 128, torch.bfloat16, 1, 4),
+                                        (4097, 24, torch.bfloat16, 1, 17),
+                                        (65536, 1024, torch.bfloat16, 4, 1024)):
         vec = 4 if dt == torch.float32 else 8
         cv = N // vec if N % vec == 0 else N          # 16-byte vector columns
         tx = 1
         while tx < 32 and tx < cv:
             tx *= 2
         assert -(-cv // tx) == strips
-        unit = max(64, 8 * (256 // tx))               # rows per unit: whole 8-row passes
-        nunits = -(-M // unit)
         got = b(M, N, dt) // (2 * N * 4)
         assert got == walkers, (M, N, dt, got)
+        unit = max(64, 8 * (256 // tx))               # rows per unit: whole 8-row passes
+        nunits = -(-M // unit)
+        if strips * nunits <= 4096:                   # small batch: one 4-row pass per unit
+            assert got == min(-(-M // (4 * (256 // tx))), 4096 // strips)
+            continue
         assert got == nunits or (got & (got - 1)) == 0    # a power of two, or every unit
         assert strips * got >= 1024 or got == nunits
         assert strips * got < 8 * max(1024, strips)
