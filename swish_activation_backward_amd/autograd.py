@@ -5,8 +5,9 @@ feed-forward gate whose forward and backward both run in the library's kernels.
 
 Forward: ``swiglu_fwd`` (g, fc and y from one fused GEMM); g and fc are saved for the
 backward, which runs the three stages of the Fused SwiGLU backward page's call chain
-(b -> w -> x): ``swiglu_bwd_b`` (dg, dfc, db), ``swiglu_bwd_w`` (dW) and ``swiglu_bwd_x``
-(dx).  The pattern is a custom operator whose backward hook calls a hand-written gradient
+(b -> w -> x): ``swiglu_bwd_b`` (dg, dfc, db), then, when both dW and dx are needed in
+bf16 or fp16, the fused ``swiglu_bwd_wx`` (both GEMMs over [dg | dfc] from one launch),
+otherwise ``swiglu_bwd_w`` (dW) and ``swiglu_bwd_x`` (dx).  The pattern is a custom operator whose backward hook calls a hand-written gradient
 kernel (the Ascend C custom-backward page, "突破自动微分瓶颈: 基于 Ascend C 的高性能自定义反向传播
 算子实战", section 4.2, Python-side registration); the weight layout [K, N] is the SwiGLU
 page's.  Leading dimensions of x are flattened into M.
@@ -46,7 +47,15 @@ class SwiGLUFunction(torch.autograd.Function):
         db_fc = torch.zeros_like(db_g)
         _lib.swiglu_bwd_b(dy, g, fc, dg, dfc, db_g, db_fc)
         dx = dw_g = dw_fc = None
-        if ctx.needs_input_grad[1] or ctx.needs_input_grad[2]:
+        need_w = ctx.needs_input_grad[1] or ctx.needs_input_grad[2]
+        if need_w and ctx.needs_input_grad[0] and g.dtype != torch.float32:
+            dw_g = torch.zeros(K, N, dtype=g.dtype, device=g.device)
+            dw_fc = torch.zeros_like(dw_g)
+            dx = torch.empty(M, K, dtype=x.dtype, device=x.device)
+            _lib.swiglu_bwd_wx(x, dg, dfc, w_g, w_fc, dw_g, dw_fc, dx)
+            return (dx, dw_g, dw_fc, db_g if ctx.has_bias[0] else None,
+                    db_fc if ctx.has_bias[1] else None)
+        if need_w:
             dw_g = torch.zeros(K, N, dtype=g.dtype, device=g.device)
             dw_fc = torch.zeros_like(dw_g)
             _lib.swiglu_bwd_w(x, dg, dfc, dw_g, dw_fc)
