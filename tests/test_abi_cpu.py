@@ -354,6 +354,38 @@ def test_fused_plan_runs_large_unsplit_shapes_as_two_stages():
     assert wx(2048, 4096, 4096, bf) == 0 and t("wx", 2048, 4096, 4096, bf) == 256
 
 
+def test_gemm_plan_invariants_over_random_shapes():
+    """Over seeded shapes (through the public queries only): the tile is 128 or 256; the
+    w stage's M splits (workspace / (K * 2N * 4 bytes)) keep tiles x splits within one
+    round of 256 workgroups, leave every split at least 512 rows and appear only when
+    the tile grid is short of 256; the fused pass's workspace is its splits' or, when it
+    runs the two stages, the w stage's; every query agrees between two calls."""
+    import numpy as np
+    import torch
+    bf = torch.bfloat16
+    rng = np.random.default_rng(77)
+    for _ in range(400):
+        M = int(rng.integers(1, 300000))
+        K = int(rng.integers(1, 600)) * 8
+        N = int(rng.integers(1, 2000)) * 8
+        per_split = K * 2 * N * 4
+        for stage in ("w", "x", "wx"):
+            e = swg.swiglu_bwd_gemm_tile(stage, M, K, N, bf)
+            assert e in (128, 256), (stage, M, K, N, e)
+        e = swg.swiglu_bwd_gemm_tile("w", M, K, N, bf)
+        tiles = -(-K // e) * 2 * -(-N // e)
+        ws = swg.swiglu_bwd_w_workspace_size(M, K, N, bf)
+        assert ws % per_split == 0
+        splits = ws // per_split
+        if splits:
+            assert splits >= 2 and tiles * splits <= 256 and tiles < 256, (M, K, N, splits)
+            assert M // splits >= 512 - 32, (M, K, N, splits)   # rows per split, 32-rounded
+        wx = swg.swiglu_bwd_wx_workspace_size(M, K, N, bf)
+        assert wx % per_split == 0 and wx // per_split <= 256
+        assert wx == swg.swiglu_bwd_wx_workspace_size(M, K, N, bf)
+        assert ws == swg.swiglu_bwd_w_workspace_size(M, K, N, bf)
+
+
 def test_workspace_queries():
     import torch
     b = swg.swiglu_bwd_b_workspace_size
