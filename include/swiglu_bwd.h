@@ -170,8 +170,9 @@ swg_status swg_set_gemm_tile(int edge);
  * bit.  Shapes whose dW grid needs no M split and where each stage alone fills the GPU
  * (e.g. M = 16384, K = 4096, N = 14336) gain nothing from sharing rows: there the call runs
  * swiglu_bwd_w and then swiglu_bwd_x (two launches on the stream, the same bits as those
- * calls).  dtype bf16 or fp16 (fp32: SWG_ERR_UNSUPPORTED); the shape and alignment rules of
- * swiglu_bwd_w and swiglu_bwd_x; dx, dw_g, dw_fc and the workspace may not overlap each
+ * calls).  dtype bf16, fp16 or fp32 (fp32 has no fused kernel: the call runs the fp32
+ * swiglu_bwd_w and then swiglu_bwd_x); the shape and alignment rules of swiglu_bwd_w and
+ * swiglu_bwd_x; dx, dw_g, dw_fc and the workspace may not overlap each
  * other or an input (SWG_ERR_INVALID).  `workspace`: swiglu_bwd_wx_workspace_size(M, K, N,
  * dtype) bytes (S * K * 2N fp32 partials; 0 when S = 1).  N = 0 writes dx = 0 (the
  * inputs and dW, all empty, may then be NULL).

@@ -5,9 +5,9 @@ feed-forward gate whose forward and backward both run in the library's kernels.
 
 Forward: ``swiglu_fwd`` (g, fc and y from one fused GEMM); g and fc are saved for the
 backward, which runs the three stages of the Fused SwiGLU backward page's call chain
-(b -> w -> x): ``swiglu_bwd_b`` (dg, dfc, db), then, when both dW and dx are needed in
-bf16 or fp16, the fused ``swiglu_bwd_wx`` (both GEMMs over [dg | dfc] from one launch),
-otherwise ``swiglu_bwd_w`` (dW) and ``swiglu_bwd_x`` (dx).  The pattern is a custom operator whose backward hook calls a hand-written gradient
+(b -> w -> x): ``swiglu_bwd_b`` (dg, dfc, db), then, when both dW and dx are needed, the
+fused ``swiglu_bwd_wx`` (both GEMMs over [dg | dfc] from one launch in bf16 / fp16),
+otherwise ``swiglu_bwd_w`` (dW) or ``swiglu_bwd_x`` (dx).  The pattern is a custom operator whose backward hook calls a hand-written gradient
 kernel (the Ascend C custom-backward page, "突破自动微分瓶颈: 基于 Ascend C 的高性能自定义反向传播
 算子实战", section 4.2, Python-side registration); the weight layout [K, N] is the SwiGLU
 page's.  Leading dimensions of x are flattened into M.
@@ -48,7 +48,7 @@ class SwiGLUFunction(torch.autograd.Function):
         _lib.swiglu_bwd_b(dy, g, fc, dg, dfc, db_g, db_fc)
         dx = dw_g = dw_fc = None
         need_w = ctx.needs_input_grad[1] or ctx.needs_input_grad[2]
-        if need_w and ctx.needs_input_grad[0] and g.dtype != torch.float32:
+        if need_w and ctx.needs_input_grad[0]:
             dw_g = torch.zeros(K, N, dtype=g.dtype, device=g.device)
             dw_fc = torch.zeros_like(dw_g)
             dx = torch.empty(M, K, dtype=x.dtype, device=x.device)

@@ -430,11 +430,19 @@ int swiglu_bwd_gemm_tile(int stage, int64_t M, int64_t K, int64_t N, swg_dtype d
 }
 
 // ------------------------------------------------------------------- fused w + x
+// fp32 has no fused kernel: it always runs the two stages (the fp32 w and x kernels)
+static WXPlan wx_plan(int dtype, int64_t M, int64_t K, int64_t N) {
+  WXPlan p = plan_wx(M, K, N, g_tile_f);
+  if (dtype == SWG_FP32) {
+    p.separate = true;
+    p.ws_bytes = plan_w(M, K, N, g_tile_f).ws_bytes;
+  }
+  return p;
+}
+
 size_t swiglu_bwd_wx_workspace_size(int64_t M, int64_t K, int64_t N, swg_dtype dtype) {
-  if (dtype == SWG_FP32 || gemm_shape_check(dtype, M, K, N) != SWG_OK || M == 0 || K == 0 ||
-      N == 0)
-    return 0;
-  return plan_wx(M, K, N, g_tile_f).ws_bytes;
+  if (gemm_shape_check(dtype, M, K, N, true) != SWG_OK || M == 0 || K == 0 || N == 0) return 0;
+  return wx_plan(dtype, M, K, N).ws_bytes;
 }
 
 swg_status swiglu_bwd_wx(const void* x, const void* dg, const void* dfc, const void* w_g,
@@ -442,7 +450,7 @@ swg_status swiglu_bwd_wx(const void* x, const void* dg, const void* dfc, const v
                          int64_t K, int64_t N, swg_dtype dtype, void* workspace,
                          size_t workspace_bytes, void* stream) {
   TimedCall timed_;
-  swg_status st = gemm_shape_check(dtype, M, K, N);   // bf16 / fp16 only
+  swg_status st = gemm_shape_check(dtype, M, K, N, true);
   if (st != SWG_OK) return st;
   if (M == 0 || K == 0) return SWG_OK;   // dx and dW are empty
   if (!dx) return SWG_ERR_NULLPTR;
@@ -454,7 +462,7 @@ swg_status swiglu_bwd_wx(const void* x, const void* dg, const void* dfc, const v
   for (const void* p : {(const void*)dw_g, (const void*)dw_fc})
     if (!aligned(p, 8)) return SWG_ERR_UNSUPPORTED;
   for (const void* p : {x, dg, dfc, w_g, w_fc}) if (!aligned(p, 16)) return SWG_ERR_UNSUPPORTED;
-  const WXPlan p = plan_wx(M, K, N, g_tile_f);
+  const WXPlan p = wx_plan(dtype, M, K, N);
   if (workspace_bytes < p.ws_bytes) return SWG_ERR_WORKSPACE;
   if (p.ws_bytes > 0 && workspace == nullptr) return SWG_ERR_NULLPTR;
   if (!aligned(workspace, 16)) return SWG_ERR_INVALID;

@@ -190,7 +190,8 @@ def test_fused_wx_argument_errors(lib):
     M, K, N = 4096, 64, 128
     need = swg.swiglu_bwd_wx_workspace_size(M, K, N, torch.bfloat16)
     assert need == swg.swiglu_bwd_wx_workspace_size(M, K, N, torch.float16)
-    assert swg.swiglu_bwd_wx_workspace_size(M, K, N, torch.float32) == 0
+    need32 = swg.swiglu_bwd_wx_workspace_size(M, K, N, torch.float32)
+    assert need32 == swg.swiglu_bwd_w_workspace_size(M, K, N, torch.float32) > 0
     W_ = ctypes.c_void_p(0x80000)
     fa = lambda **kw: [kw.get(k, d) for k, d in  # noqa: E731
                        (("x", P), ("dg", Q), ("dfc", R), ("wg", S), ("wfc", T), ("dwg", U),
@@ -201,7 +202,8 @@ def test_fused_wx_argument_errors(lib):
     assert f(*fa(K=0, dx=NULL)) == OK
     assert f(*fa(M=-1)) == INVALID
     assert f(*fa(dt=9)) == INVALID
-    assert f(*fa(dt=FP32)) == UNSUPPORTED            # 16-bit only
+    assert f(*fa(dt=FP32, K=66)) == UNSUPPORTED      # fp32: K, N multiples of 4
+    assert f(*fa(dt=FP32, wb=need32 - 1)) == WORKSPACE   # fp32 runs w then x
     assert f(*fa(K=60)) == UNSUPPORTED
     assert f(*fa(N=100)) == UNSUPPORTED
     for k in ("x", "dg", "dfc", "wg", "wfc", "dwg", "dwfc", "dx"):

@@ -125,7 +125,35 @@ def test_fused_large_unsplit_shape_runs_the_two_stages():
     compare("dx rows", fdx.cpu()[rows], ref, "bf16", model_abs=sum_abs_model(a))
 
 
-def test_fused_empty_contraction_and_fp32():
+def test_fused_fp32_runs_the_two_stages():
+    """fp32 has no fused kernel: the call runs the fp32 w and x stages, bit-identical to
+    swiglu_bwd_w and swiglu_bwd_x, and matches the oracle (tiny and an odd ragged shape)."""
+    dev = device()
+    for (M, K, N) in ((256, 64, 128), (1001, 132, 260)):
+        inp = swiglu_inputs(SwiGLUShape("f32wx", 27, M, K, N), dtype="fp32")
+        dg, dfc = _oracle_dg(inp, "fp32")
+        d = {k: v.to(dev) for k, v in (("x", inp["x"]), ("dg", dg), ("dfc", dfc),
+                                       ("w_g", inp["w_g"]), ("w_fc", inp["w_fc"]))}
+        note(f"fused w+x fp32 M={M} K={K} N={N}")
+        f = torch.float32
+        fdw_g, fdw_fc = torch.zeros(K, N, dtype=f, device=dev), torch.zeros(K, N, dtype=f, device=dev)
+        fdx = torch.empty(M, K, dtype=f, device=dev)
+        swg.swiglu_bwd_wx(d["x"], d["dg"], d["dfc"], d["w_g"], d["w_fc"], fdw_g, fdw_fc, fdx)
+        sdw_g, sdw_fc = torch.zeros_like(fdw_g), torch.zeros_like(fdw_fc)
+        sdx = torch.empty_like(fdx)
+        swg.swiglu_bwd_w(d["x"], d["dg"], d["dfc"], sdw_g, sdw_fc)
+        swg.swiglu_bwd_x(d["dg"], d["dfc"], d["w_g"], d["w_fc"], sdx)
+        torch.cuda.synchronize()
+        for name, a, b in (("dw_g", fdw_g, sdw_g), ("dw_fc", fdw_fc, sdw_fc), ("dx", fdx, sdx)):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+        rg, rf, ag, af = oracle_w_chunked(inp["x"], dg, dfc)
+        compare("fp32 fused dw_g", fdw_g.cpu(), rg, "fp32", model_abs=sum_abs_model(ag))
+        compare("fp32 fused dw_fc", fdw_fc.cpu(), rf, "fp32", model_abs=sum_abs_model(af))
+        ref, a = oracle_x_rows(dg, dfc, inp["w_g"], inp["w_fc"], slice(None))
+        compare("fp32 fused dx", fdx.cpu(), ref, "fp32", model_abs=sum_abs_model(a))
+
+
+def test_fused_empty_contraction():
     dev = device()
     M, K = 33, 16
     bf = torch.bfloat16
@@ -137,6 +165,3 @@ def test_fused_empty_contraction_and_fp32():
     swg.swiglu_bwd_wx(x, e, e, w, w, w.clone(), w.clone(), dx)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dx).item() == 0
-    f = torch.float32
-    with pytest.raises(swg.SwgError):
-        swg.swiglu_bwd_wx(x.to(f), e.to(f), e.to(f), w.to(f), w.to(f), w.to(f), w.to(f), dx.to(f))
