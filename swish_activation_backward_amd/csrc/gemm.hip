@@ -6,7 +6,9 @@
 //
 // Both kernels compute a 256 x 256 output tile per workgroup of four wavefronts (one
 // per SIMD); each wave owns a 128 x 128 block = 4 x 4 tiles of v_mfma_f32_32x32x16 whose
-// 256 fp32 accumulators live in the AGPR file.
+// 256 fp32 accumulators live in the AGPR file.  A second configuration halves every edge
+// (128 x 128 tiles, 64 x 64 per wave) for outputs that 256 x 256 tiles would spread over
+// too few CUs (see Tc below).
 //
 // Operands move global -> LDS with buffer_load ... lds (the load unit writes LDS
 // directly; no registers, no ds_write), and operand fragments are double-buffered in
@@ -153,8 +155,8 @@ __device__ inline void zero_acc(f32x16 (&acc)[F][F]) {
 // 8 (l / 32) .. 8 (l / 32) + 7 of each operand; accumulator register r of lane l holds
 // row 8 (r / 4) + 4 (l / 32) + (r % 4), column l % 32.
 
-// ------------------------------------------------------------------ x-stage tiles
-// Slot layout: [256 rows of A][32] then [256 rows of B][32]; a row is 4 chunks of 16 B.
+// ------------------------------------------------------------------ 32-deep row tiles
+// (the forward's x operand) Slot layout: [256 rows][32]; a row is 4 chunks of 16 B.
 // Chunk c of row r sits at position c ^ xsw(r), xsw(r) = (r / 4) % 4: within 16
 // consecutive rows (one group of 16 lanes of a 16-byte read) the four rows that share a
 // 64-byte bank window take four different chunks (measured: full LDS read rate, no bank
@@ -432,8 +434,8 @@ __device__ inline void store_tile_rows(const f32x16 (&acc)[F][F], int lane,
 // ----------------------------------------------------------------- x stage (NT)
 // A = [dg | dfc] rows p (M), B = [W_g | W_fc] rows q (K).  Double stage d < sD contracts
 // over columns 64 d .. of dg / W_g, d >= sD over the same columns of dfc / W_fc
-// (sD = max(2, ceil(N / 64)); columns past N read zeros).  Tile L covers rows (L / nq) * 256
-// and columns (L % nq) * 256.
+// (sD = max(2, ceil(N / 64)); columns past N read zeros).  Tile L covers rows (L / nq) * P
+// and columns (L % nq) * P (P = 256 or 128).
 //
 // Two steps per double stage d (stages t = 2d, 2d + 1):
 //   even t: read stage t + 1 (the second halves of the A and B slots of double stage d,
@@ -741,7 +743,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(Tc<F>::XOCC,
 
 // ----------------------------------------------------------------- w stage (TN)
 // A = x^T: rows k (K), contraction m;  B = d^T (d = dg or dfc): rows n, contraction m.
-// Work item L = (split s, tile tt): output rows k0 = (tt / (2 tnh)) * 256, columns n0 of
+// Work item L = (split s, tile tt): output rows k0 = (tt / (2 tnh)) * P, columns n0 of
 // dg (tt % (2 tnh) < tnh) or of dfc, contracting over the rows of split s.  A split's rows
 // are either one range [s R, min(M, (s + 1) R)) (the w stage) or chunks of CH rows taken
 // every S chunks: chunk j of split s covers rows (s + j S) CH .. (the fused pass, whose
