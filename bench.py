@@ -240,7 +240,6 @@ def time_configs(swg, names=("tiny", "ragged", "llm_ffn"), warmup=3, steps=10):
     import torch
     from workloads.gen import SWIGLU_WORKLOADS, swiglu_inputs
     dev = torch.device("cuda", 0)
-    stream = torch.cuda.current_stream()
     evict = Evictor(dev)
     res = {}
     for name in names:
@@ -335,8 +334,6 @@ def copy_calibration(nbytes, reps=5):
 
 def cpu_baseline(inp, sw_inputs, rows, swish_len):
     """The float64 oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np
-
     import oracle.ref as R
     try:
         from threadpoolctl import threadpool_info
