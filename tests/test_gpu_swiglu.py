@@ -200,6 +200,40 @@ def test_gemm_stages_random_shapes(seed, tile):
 
 
 @pytest.mark.parametrize("seed", range(6))
+def test_gemm_stages_large_random_shapes(seed, tile):
+    """Seeded larger shapes (M up to 60000, K and N up to 4096, ragged edges) at both tile
+    sizes: w on 96 sampled columns of dW, x on 192 sampled rows of dx, against the oracle."""
+    rng = np.random.default_rng(5000 + seed)
+    M = int(rng.integers(1000, 60000))
+    K = int(rng.integers(1, 4096 // 8 + 1)) * 8
+    N = int(rng.integers(1, 4096 // 8 + 1)) * 8
+    dt = "bf16" if seed % 2 == 0 else "fp16"
+    dev = device()
+    tdt = DTYPES[dt]
+    g = torch.Generator().manual_seed(6000 + seed)
+    r = lambda *s, sc: (torch.randn(*s, generator=g) * sc).to(tdt)  # noqa: E731
+    x, dg, dfc = r(M, K, sc=M ** -0.5), r(M, N, sc=1e-2), r(M, N, sc=1e-2)
+    w_g, w_fc = r(K, N, sc=K ** -0.5), r(K, N, sc=K ** -0.5)
+    note(f"large random gemm M={M} K={K} N={N} {dt} tile {tile}")
+    dw_g, dw_fc = Guarded((K, N), tdt, dev, fill=torch.zeros(K, N, dtype=tdt, device=dev)), \
+        Guarded((K, N), tdt, dev, fill=torch.zeros(K, N, dtype=tdt, device=dev))
+    dx = Guarded((M, K), tdt, dev)
+    d = {k: v.to(dev) for k, v in (("x", x), ("dg", dg), ("dfc", dfc), ("w_g", w_g), ("w_fc", w_fc))}
+    swg.swiglu_bwd_w(d["x"], d["dg"], d["dfc"], dw_g.t, dw_fc.t)
+    swg.swiglu_bwd_x(d["dg"], d["dfc"], d["w_g"], d["w_fc"], dx.t)
+    torch.cuda.synchronize()
+    for buf in (dw_g, dw_fc, dx):
+        buf.check()
+    cols = np.sort(rng.choice(N, min(N, 96), replace=False))
+    rows = np.sort(rng.choice(M, min(M, 192), replace=False))
+    rg, rf, ag, af = oracle_w_chunked(x, dg, dfc, cols=cols)
+    compare("dw_g cols", dw_g.t.cpu()[:, cols], rg, dt, model_abs=sum_abs_model(ag))
+    compare("dw_fc cols", dw_fc.t.cpu()[:, cols], rf, dt, model_abs=sum_abs_model(af))
+    ref, a = oracle_x_rows(dg, dfc, w_g, w_fc, rows)
+    compare("dx rows", dx.t.cpu()[rows], ref, dt, model_abs=sum_abs_model(a))
+
+
+@pytest.mark.parametrize("seed", range(6))
 def test_gemm_stages_fp32_random_shapes(seed):
     M, K, N = _random_shape(100 + seed, 4)
     inp = swiglu_inputs(SwiGLUShape("rand32", 60 + seed, M, K, N), dtype="fp32")
