@@ -557,7 +557,7 @@ __device__ inline void x_read_one(const uint16_t* aslot, const uint16_t* bslot, 
   using Fr = typename Mfma<T>::frag;
   constexpr int kk = G / (2 * F), idx = G % (2 * F);
   const int lc = 2 * kk + (lane >> 5);
-  if (idx < F) {
+  if constexpr (idx < F) {
     const int r = wp * Tc<F>::WR + idx * 32 + (lane & 31);
     f.a[kk][idx] = *reinterpret_cast<const Fr*>(aslot + r * XA_BR + (((4 * HALF + lc) ^ xsw8(r)) << 3));
   } else {
@@ -842,7 +842,7 @@ __device__ inline void w_read_one(const uint16_t* slot, const int (&aoff)[F],
                                   const int (&boff)[F], FragSet<T, F>& f) {
   constexpr int P = Tc<F>::P;
   constexpr int ks = G / (2 * F), idx = G % (2 * F);
-  if (idx < F) f.a[ks][idx] = tr_frag<T, P>(slot + 16 * ks * P + aoff[idx]);
+  if constexpr (idx < F) f.a[ks][idx] = tr_frag<T, P>(slot + 16 * ks * P + aoff[idx]);
   else f.b[ks][idx - F] = tr_frag<T, P>(slot + BR * P + 16 * ks * P + boff[idx - F]);
 }
 
