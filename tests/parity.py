@@ -80,6 +80,20 @@ def sum_abs_model(abs_sum):
     return 2.0 ** -16 * np.asarray(abs_sum, dtype=np.float64)
 
 
+def forward_abs_models(x, w_g, w_fc, b_g, b_fc, g, fc):
+    """Rounding models of a correct kernel: fp32 accumulation of g and fc (2^-16 times the
+    magnitude sums, bias included) and their propagation into y = g sigma(g) fc, plus the
+    fp32 evaluation of y itself."""
+    ax = np.abs(to64(x))
+    ag = ax @ np.abs(to64(w_g)) + (0.0 if b_g is None else np.abs(to64(b_g)))
+    af = ax @ np.abs(to64(w_fc)) + (0.0 if b_fc is None else np.abs(to64(b_fc)))
+    eg, ef = sum_abs_model(ag), sum_abs_model(af)
+    s = _sig(g)
+    ds = np.abs(s + g * s * (1.0 - s))          # d SiLU / d g
+    ey = ds * np.abs(fc) * eg + np.abs(g * s) * ef + 8.0 * U32 * np.abs(g * s * fc)
+    return eg, ef, ey
+
+
 def chained_abs_model(abs_sum, dtype):
     """A sum of products whose operand was itself a rounded output of an earlier stage
     (the w and x stages fed by the b stage's dg and dfc, stored in ``dtype``): each operand

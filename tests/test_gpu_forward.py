@@ -11,7 +11,7 @@ import torch
 import oracle.ref as R
 import swish_activation_backward_amd as swg
 from gpu_util import Guarded, device, note
-from parity import U32, compare, sum_abs_model, to64
+from parity import U32, compare, forward_abs_models, sum_abs_model, to64
 from workloads.gen import DTYPES, SWIGLU_WORKLOADS, SwiGLUShape, swiglu_inputs
 
 pytestmark = pytest.mark.gpu
@@ -20,20 +20,6 @@ pytestmark = pytest.mark.gpu
 def _sig(t):
     with np.errstate(over="ignore"):
         return 1.0 / (1.0 + np.exp(-t))
-
-
-def _models(x, w_g, w_fc, b_g, b_fc, g, fc):
-    """Rounding models of a correct kernel: fp32 accumulation of g and fc (2^-16 times the
-    magnitude sums, bias included) and their propagation into y = g sigma(g) fc, plus the
-    fp32 evaluation of y itself."""
-    ax = np.abs(to64(x))
-    ag = ax @ np.abs(to64(w_g)) + (0.0 if b_g is None else np.abs(to64(b_g)))
-    af = ax @ np.abs(to64(w_fc)) + (0.0 if b_fc is None else np.abs(to64(b_fc)))
-    eg, ef = sum_abs_model(ag), sum_abs_model(af)
-    s = _sig(g)
-    ds = np.abs(s + g * s * (1.0 - s))          # d SiLU / d g
-    ey = ds * np.abs(fc) * eg + np.abs(g * s) * ef + 8.0 * U32 * np.abs(g * s * fc)
-    return eg, ef, ey
 
 
 def _fwd_case(inp, dt, bias=True, rows=None):
@@ -56,7 +42,7 @@ def _fwd_case(inp, dt, bias=True, rows=None):
     zero = np.zeros(N)
     rg, rf, ry = R.swiglu_forward_ref(xr, to64(w_g), zero if b_g is None else to64(b_g),
                                       to64(w_fc), zero if b_fc is None else to64(b_fc))
-    eg, ef, ey = _models(xr, w_g, w_fc, b_g, b_fc, rg, rf)
+    eg, ef, ey = forward_abs_models(xr, w_g, w_fc, b_g, b_fc, rg, rf)
     compare("g", g.t.cpu()[sel], rg, dt, model_abs=eg)
     compare("fc", fc.t.cpu()[sel], rf, dt, model_abs=ef)
     compare("y", y.t.cpu()[sel], ry, dt, model_abs=ey)

@@ -1,5 +1,5 @@
 """GPU parity past 2^31 elements per tensor: the b stage, the w and x stages, the fused
-w + x pass and swish_grad on tensors whose element offsets do not fit 32 bits (and, for
+w + x pass, the forward and swish_grad on tensors whose element offsets do not fit 32 bits (and, for
 swish_grad, long enough that its grid strides: more than 2^20 workgroups of vectors).
 
 Inputs are a seeded block of P rows (P odd, so no 2^k-element wrap of an offset lands on
@@ -21,7 +21,7 @@ import torch
 import oracle.ref as R
 import swish_activation_backward_amd as swg
 from gpu_util import device, note, oracle_b_chunked, oracle_w_chunked, oracle_x_rows
-from parity import compare, sum_abs_model, swish_abs_model
+from parity import compare, forward_abs_models, sum_abs_model, swish_abs_model, to64
 from workloads.gen import DTYPES, SwiGLUShape, swiglu_inputs, swish_inputs
 
 pytestmark = pytest.mark.gpu
@@ -30,6 +30,7 @@ TWO31 = 1 << 31
 # (P, M, N) of the b-stage case, (P, M, K, N) of the GEMM case, P of the swish_grad cases
 B_CASE = (4099, (1 << 21) + 77, 1048)
 GEMM_CASE = (4099, (1 << 20) + 77, 2048, 512)
+FWD_CASE = (4099, (1 << 20) + 77, 2048, 2048)
 SWISH_P = 1000003
 SWISH_CASES = [("bf16", TWO31 + (1 << 21) + 37), ("fp32", (1 << 30) + (1 << 20) + 5)]
 
@@ -144,6 +145,32 @@ def test_gemm_stages_past_2_31_elements():
         compare(f"fused {name}", got.cpu(), want[name][0], dt,
                 model_abs=sum_abs_model(want[name][1]))
     del x, dg, dfc, dx, dx2
+    torch.cuda.empty_cache()
+
+
+def test_forward_past_2_31_elements():
+    """x, g, fc and y of M = 2^20 + 77 rows by 2048 columns (2.1e9 elements each), bf16."""
+    dev = device()
+    (P, M, K, N), dt = FWD_CASE, "bf16"
+    assert M * K > TWO31 and M * N > TWO31
+    _need(M * K * 2 + 3 * M * N * 2 + (1 << 30))
+    tdt = DTYPES[dt]
+    blk = swiglu_inputs(SwiGLUShape("large_fwd", 53, P, K, N), dtype=dt, with_forward=False)
+    x = _tile_rows(blk["x"], M, dev)
+    g, fc, y = (torch.empty(M, N, dtype=tdt, device=dev) for _ in range(3))
+    note(f"forward M={M} K={K} N={N} {dt} (2^31+ elements)")
+    swg.swiglu_fwd(x, blk["w_g"].to(dev), blk["w_fc"].to(dev), blk["b_g"].to(dev),
+                   blk["b_fc"].to(dev), g, fc, y)
+    torch.cuda.synchronize()
+    del x
+    xr = to64(blk["x"])
+    rg, rf, ry = R.swiglu_forward_ref(xr, to64(blk["w_g"]), to64(blk["b_g"]), to64(blk["w_fc"]),
+                                      to64(blk["b_fc"]))
+    eg, ef, ey = forward_abs_models(xr, blk["w_g"], blk["w_fc"], blk["b_g"], blk["b_fc"], rg, rf)
+    for name, t, ref, model in (("g", g, rg, eg), ("fc", fc, rf, ef), ("y", y, ry, ey)):
+        compare(f"{name}[:P]", t[:P].cpu(), ref, dt, model_abs=model)
+        _assert_periodic(name, t, P)
+    del g, fc, y
     torch.cuda.empty_cache()
 
 
