@@ -50,6 +50,10 @@ def _sig(t):
 
 
 FP32_TINY = 2.0 ** -126   # smallest normal fp32: hardware exp may flush below it
+# Absolute floor of a correct result's last rounding below the smallest normal: half the
+# fp16 subnormal spacing; for fp32, a result under 2^-126 rounded to the subnormal grid
+# (error <= 2^-150) or flushed to zero (error < 2^-126).  bf16 results carry atol 1e-4.
+SUBNORMAL_FLOOR = {"bf16": 0.0, "fp16": FP16_SUBNORMAL_HALF, "fp32": FP32_TINY}
 
 
 def swish_abs_model(grad, x, beta):
@@ -130,14 +134,12 @@ class Checker:
             atol = BF16_ATOL
         else:
             atol = 0.0 if model_abs is None else model_abs
-            if self.dtype == "fp16":
-                atol = atol + FP16_SUBNORMAL_HALF
+            atol = atol + SUBNORMAL_FLOOR[self.dtype]
         self.n += r.size
         self.nonfinite += int((~np.isfinite(g)).sum())
         self.contract_fail += int((err > atol + self.rtol * absr).sum())
         if model_abs is not None:
-            extra = FP16_SUBNORMAL_HALF if self.dtype == "fp16" else 0.0
-            bound = self.rtol * absr + model_abs + extra
+            bound = self.rtol * absr + model_abs + SUBNORMAL_FLOOR[self.dtype]
             self.mixed_fail += int((err > bound).sum())
         self.ss_ref += float(np.sum(r * r))
         self.ss_err += float(np.sum(err * err))

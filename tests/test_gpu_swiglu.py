@@ -301,6 +301,79 @@ def test_chained_b_w_x_on_ragged_batch():
         compare(f"chained {k}", v.cpu(), ref[k], "bf16", model_abs=models[k])
 
 
+# Gate values from the saturated tails to zero, within each dtype's finite range: sigma
+# and 1 - sigma underflow (g -> -inf: dg -> 0, dfc -> 0) or reach 1 and 0 (g -> +inf:
+# dg -> dy fc, dfc -> dy g), and g = +-0 gives dg = dy fc / 2, dfc = 0.
+_EXTREME_G = {
+    "bf16": [-3.0e38, -1.0e4, -700.0, -100.0, -88.5, -30.0, -17.0, -1e-30, -0.0,
+             0.0, 1e-30, 17.0, 30.0, 88.5, 100.0, 700.0, 1.0e4, 3.0e38],
+    "fp16": [-6.0e4, -1.0e4, -700.0, -100.0, -88.5, -30.0, -17.0, -1e-7, -0.0,
+             0.0, 1e-7, 17.0, 30.0, 88.5, 100.0, 700.0, 1.0e4, 6.0e4],
+    "fp32": [-3.0e38, -1.0e4, -700.0, -100.0, -88.5, -30.0, -17.0, -1e-40, -0.0,
+             0.0, 1e-40, 17.0, 30.0, 88.5, 100.0, 700.0, 1.0e4, 3.0e38],
+}
+
+
+def _extreme_b_inputs(dt, M=257, N=144, seed=61):
+    """dy ~ N(0,1) 1e-3 and fc ~ N(0,1); every row of g a seeded arrangement of the
+    extreme gate values (so dfc = dy g sigma(g) stays finite: |dy g| < 1e36)."""
+    gen = torch.Generator().manual_seed(seed)
+    vals = torch.tensor(_EXTREME_G[dt], dtype=torch.float64)
+    idx = torch.randint(0, len(vals), (M, N), generator=gen)
+    tdt = DTYPES[dt]
+    return {"dy": (torch.randn(M, N, generator=gen) * 1e-3).to(tdt),
+            "g": vals[idx].to(tdt),
+            "fc": torch.randn(M, N, generator=gen).to(tdt)}
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+def test_b_stage_saturated_gate_values(dt):
+    """Extreme but finite g: outputs finite and within the tolerances of the oracle."""
+    _b_case(_extreme_b_inputs(dt), dt)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+def test_b_stage_non_finite_gate_values(dt):
+    """g = +-inf or NaN in a few positions: dg and dfc are NaN or +-inf exactly where the
+    oracle's float64 values are (SiLU'(+-inf) takes inf * 0 = NaN, as torch's
+    silu_backward does; dfc = dy * (+inf) * 1 = +-inf, dy * (-inf) * 0 = NaN), and every
+    other element and every column sum of finite columns matches the oracle."""
+    dev = device()
+    inp = _extreme_b_inputs(dt, M=129, N=64, seed=62)
+    g = inp["g"].clone()
+    bad = [(0, 0, float("inf")), (5, 9, float("-inf")), (64, 17, float("nan")),
+           (128, 63, float("nan"))]
+    for r, c, v in bad:
+        g[r, c] = v
+    inp["g"] = g
+    M, N = g.shape
+    tdt = DTYPES[dt]
+    dy, gg, fc = (inp[k].to(dev) for k in ("dy", "g", "fc"))
+    dg, dfc = torch.empty_like(dy), torch.empty_like(dy)
+    db_g, db_fc = torch.zeros(N, dtype=tdt, device=dev), torch.zeros(N, dtype=tdt, device=dev)
+    note(f"b stage non-finite g {dt}")
+    swg.swiglu_bwd_b(dy, gg, fc, dg, dfc, db_g, db_fc)
+    torch.cuda.synchronize()
+    dy64, g64, fc64 = to64(inp["dy"]), to64(g), to64(inp["fc"])
+    with np.errstate(all="ignore"):
+        rdg, rdfc, rbg, rbf = R.b_ref(dy64, g64, fc64)
+        models = {"dg": dg_abs_model(dy64, g64, fc64), "dfc": dfc_abs_model(dy64, g64)}
+    for name, got, ref in (("dg", dg, rdg), ("dfc", dfc, rdfc), ("db_g", db_g, rbg),
+                           ("db_fc", db_fc, rbf)):
+        got = to64(got.cpu())
+        fin = np.isfinite(ref)
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), f"{name}: NaN positions"
+        assert np.array_equal(np.isposinf(got), np.isposinf(ref)), f"{name}: +inf positions"
+        assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{name}: -inf positions"
+        assert (~fin).any() or name.startswith("db"), f"{name}: no non-finite case exercised"
+        if name in models:
+            compare(name, got[fin], ref[fin], dt, model_abs=models[name][fin])
+        else:
+            terms = rdg if name == "db_g" else rdfc
+            absum = np.abs(np.where(np.isfinite(terms), terms, 0.0)).sum(0)
+            compare(name, got[fin], ref[fin], dt, model_abs=sum_abs_model(absum[fin]))
+
+
 def test_bitwise_deterministic_reruns():
     dev = device()
     inp = swiglu_inputs("ragged", dtype="bf16")
