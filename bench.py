@@ -176,6 +176,53 @@ def time_fused(swg, d, dg, dfc, M, K, N, warmup, steps):
                     "inputs; compare with stages w + x; not part of the step"}
 
 
+def time_fp16(swg, d, M, K, N, warmup, steps):
+    """The b, w and x stages on fp16 copies of the step's bf16 inputs (the same values
+    rounded to fp16), each timed by its kernel span over `steps` calls after the step: the
+    fp16 path at the headline shape, for comparison with the bf16 stages (not part of the
+    step or of `value`; fp16 matrix cores have the bf16 peak)."""
+    import torch
+    h = {k: d[k].to(torch.float16) for k in ("x", "dy", "g", "fc", "w_g", "w_fc")}
+    dg, dfc = torch.empty_like(h["dy"]), torch.empty_like(h["dy"])
+    db_g = torch.zeros(N, dtype=torch.float16, device=h["x"].device)
+    db_fc = torch.zeros_like(db_g)
+    dw_g = torch.zeros(K, N, dtype=torch.float16, device=h["x"].device)
+    dw_fc = torch.zeros_like(dw_g)
+    dx = torch.empty(M, K, dtype=torch.float16, device=h["x"].device)
+    ws_b = torch.empty(max(1, swg.swiglu_bwd_b_workspace_size(M, N, torch.float16)),
+                       dtype=torch.uint8, device=h["x"].device)
+    ws_w = torch.empty(max(1, swg.swiglu_bwd_w_workspace_size(M, K, N, torch.float16)),
+                       dtype=torch.uint8, device=h["x"].device)
+    calls = {
+        "b": lambda: swg.swiglu_bwd_b(h["dy"], h["g"], h["fc"], dg, dfc, db_g, db_fc,
+                                      workspace=ws_b),
+        "w": lambda: swg.swiglu_bwd_w(h["x"], dg, dfc, dw_g, dw_fc, workspace=ws_w),
+        "x": lambda: swg.swiglu_bwd_x(dg, dfc, h["w_g"], h["w_fc"], dx),
+    }
+    work = stage_work(M, K, N, 0)
+    out = {"note": "b, w, x on fp16 copies of the step's inputs, mean kernel span; not part "
+                   "of the step"}
+    for name, f in calls.items():
+        for _ in range(warmup):
+            f()
+        timer = SpanTimer(swg, steps)
+        for i in range(steps):
+            timer.arm(i)
+            f()
+        torch.cuda.synchronize()
+        t = sum(timer.seconds(i) for i in range(steps)) / steps
+        wk = work[name]
+        e = {"us": round(t * 1e6, 2), "frac": round(wk["t_roof"] / t, 4), "bound": wk["bound"]}
+        if wk["flops"]:
+            e["TFLOP/s"] = round(wk["flops"] / t / 1e12, 1)
+        else:
+            e["GB/s"] = round(wk["bytes"] / t / 1e9, 1)
+        out[name] = e
+    del h, dg, dfc, dx, dw_g, dw_fc, ws_b, ws_w
+    torch.cuda.empty_cache()
+    return out
+
+
 class Evictor:
     """Evicts the 256 MB last-level cache before a cold timed call by reading a 1 GiB
     buffer (a read-only pass: the timed call then finds its inputs in HBM and no dirty
@@ -575,6 +622,7 @@ def main():
     out["fused_wx"] = time_fused(swg, d, dg, dfc, M, K, N, args.warmup, args.steps)
     out["fused_wx"]["unfused_w_plus_x_us"] = round(stages["w"]["us"] + stages["x"]["us"], 2)
     out["forward"] = time_forward(swg, d, M, K, N, args.warmup, args.steps)
+    out["fp16"] = time_fp16(swg, d, M, K, N, args.warmup, args.steps)
     out["swish_pages_shape"] = time_swish_context(swg, 20)
     if not args.no_per_config:
         out["per_config"] = time_configs(swg)

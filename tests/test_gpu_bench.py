@@ -47,3 +47,6 @@ def test_bench_json_line_on_the_tiny_workload():
         # the kernel span lies inside the events recorded around the call
         assert st["us"] <= st["event_us"] + 5.0, (name, st)
     assert abs(roof["avg_launch_us"] - d["stages"][roof["stage"]]["us"]) < 0.01
+    for name in ("b", "w", "x"):   # the fp16 stages timed beside the step
+        st = d["fp16"][name]
+        assert st["us"] > 0 and 0 < st["frac"] <= 1, (name, st)
