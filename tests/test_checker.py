@@ -94,3 +94,29 @@ def test_checker_accumulates_chunks(bstage):
     c2.add(np.zeros_like(dg[:10]), dg[:10])
     with pytest.raises(ParityError):
         c2.result()
+
+
+def test_fp32_contraction_normwise_bound():
+    """fp32 outputs that sum n products get the normwise bound max(2^-20, 2 u sqrt(n));
+    bf16 and fp16 keep their storage-rounding bounds.  A sum evaluated in fp32 (sequential,
+    products rounded) over 3008 random-sign terms passes with it, while 1e-4 relative noise
+    fails; the fixed fp32 bound stays 2^-20 for short sums."""
+    from parity import NORMWISE, U32, contraction_normwise, sum_abs_model
+    assert contraction_normwise("fp32", 16) == 2.0 ** -20
+    assert contraction_normwise("fp32", 3008) == pytest.approx(2 * U32 * np.sqrt(3008))
+    assert contraction_normwise("bf16", 10 ** 6) == NORMWISE["bf16"]
+    assert contraction_normwise("fp16", 10 ** 6) == NORMWISE["fp16"]
+    rng = np.random.default_rng(3)
+    n, m = 3008, 400
+    a = rng.normal(0, 1, (m, n)).astype(np.float32)
+    b = rng.normal(0, 1, n).astype(np.float32)
+    exact = a.astype(np.float64) @ b.astype(np.float64)
+    acc = np.zeros(m, dtype=np.float32)
+    for k in range(n):                        # fp32 products and fp32 running sums
+        acc = (acc + a[:, k] * b[k]).astype(np.float32)
+    model = sum_abs_model(np.abs(a.astype(np.float64)) @ np.abs(b.astype(np.float64)))
+    assert compare("fp32 sum", acc.astype(np.float64), exact, "fp32", model_abs=model,
+                   contraction=n)["ok"]
+    noisy = exact * (1 + 1e-4 * rng.choice([-1.0, 1.0], m))
+    with pytest.raises(ParityError):
+        compare("fp32 sum, noisy", noisy, exact, "fp32", model_abs=model, contraction=n)

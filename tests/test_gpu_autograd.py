@@ -54,18 +54,22 @@ def _oracle_parity(y, saved, x, w_g, w_fc, b_g, b_fc, dy, grads):
     s = _sig(rg)
     ey = (np.abs(s + rg * s * (1 - s)) * np.abs(rf) * eg + np.abs(rg * s) * ef
           + 8.0 * U32 * np.abs(rg * s * rf))
-    compare("y", y, ry, dt, model_abs=ey)
-    compare("saved g", g_s, rg, dt, model_abs=eg)
-    compare("saved fc", fc_s, rf, dt, model_abs=ef)
+    K = wg64.shape[0]
+    M = x64.reshape(-1, K).shape[0]
+    compare("y", y, ry, dt, model_abs=ey, contraction=K)
+    compare("saved g", g_s, rg, dt, model_abs=eg, contraction=K)
+    compare("saved fc", fc_s, rf, dt, model_abs=ef, contraction=K)
     ref = R.swiglu_bwd_ref(dy64, x64, wg64, wf64, g_s, fc_s)
     adg, adfc = np.abs(ref["dg"]), np.abs(ref["dfc"])
     models = {"dx": chained_abs_model(adg @ np.abs(wg64).T + adfc @ np.abs(wf64).T, dt),
               "dw_g": chained_abs_model(ax.T @ adg, dt),
               "dw_fc": chained_abs_model(ax.T @ adfc, dt),
               "db_g": sum_abs_model(adg.sum(0)), "db_fc": sum_abs_model(adfc.sum(0))}
+    terms = {"dx": 2 * N, "dw_g": M, "dw_fc": M, "db_g": M, "db_fc": M}
     for name, got in grads.items():
         if got is not None:
-            compare(f"autograd {name}", got, ref[name], dt, model_abs=models[name])
+            compare(f"autograd {name}", got, ref[name], dt, model_abs=models[name],
+                    contraction=terms[name])
 
 
 def _ref_grads(x, w_g, w_fc, b_g, b_fc, dy):

@@ -43,9 +43,9 @@ def _fwd_case(inp, dt, bias=True, rows=None):
     rg, rf, ry = R.swiglu_forward_ref(xr, to64(w_g), zero if b_g is None else to64(b_g),
                                       to64(w_fc), zero if b_fc is None else to64(b_fc))
     eg, ef, ey = forward_abs_models(xr, w_g, w_fc, b_g, b_fc, rg, rf)
-    compare("g", g.t.cpu()[sel], rg, dt, model_abs=eg)
-    compare("fc", fc.t.cpu()[sel], rf, dt, model_abs=ef)
-    compare("y", y.t.cpu()[sel], ry, dt, model_abs=ey)
+    compare("g", g.t.cpu()[sel], rg, dt, model_abs=eg, contraction=K)
+    compare("fc", fc.t.cpu()[sel], rf, dt, model_abs=ef, contraction=K)
+    compare("y", y.t.cpu()[sel], ry, dt, model_abs=ey, contraction=K)
     return g.t, fc.t, y.t
 
 

@@ -147,10 +147,13 @@ def test_fused_fp32_runs_the_two_stages():
         for name, a, b in (("dw_g", fdw_g, sdw_g), ("dw_fc", fdw_fc, sdw_fc), ("dx", fdx, sdx)):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
         rg, rf, ag, af = oracle_w_chunked(inp["x"], dg, dfc)
-        compare("fp32 fused dw_g", fdw_g.cpu(), rg, "fp32", model_abs=sum_abs_model(ag))
-        compare("fp32 fused dw_fc", fdw_fc.cpu(), rf, "fp32", model_abs=sum_abs_model(af))
+        compare("fp32 fused dw_g", fdw_g.cpu(), rg, "fp32", model_abs=sum_abs_model(ag),
+                contraction=M)
+        compare("fp32 fused dw_fc", fdw_fc.cpu(), rf, "fp32", model_abs=sum_abs_model(af),
+                contraction=M)
         ref, a = oracle_x_rows(dg, dfc, inp["w_g"], inp["w_fc"], slice(None))
-        compare("fp32 fused dx", fdx.cpu(), ref, "fp32", model_abs=sum_abs_model(a))
+        compare("fp32 fused dx", fdx.cpu(), ref, "fp32", model_abs=sum_abs_model(a),
+                contraction=2 * N)
 
 
 def test_fused_empty_contraction():

@@ -35,9 +35,9 @@ def _b_case(inp, dt, db0=None):
     res["check_dg"].result()
     res["check_dfc"].result()
     compare("db_g", db_g.t.cpu(), res["db_g"], dt,
-            model_abs=sum_abs_model(res["abs_g"] + np.abs(to64(init))))
+            model_abs=sum_abs_model(res["abs_g"] + np.abs(to64(init))), contraction=M)
     compare("db_fc", db_fc.t.cpu(), res["db_fc"], dt,
-            model_abs=sum_abs_model(res["abs_fc"] + np.abs(to64(init))))
+            model_abs=sum_abs_model(res["abs_fc"] + np.abs(to64(init))), contraction=M)
     return dg.t, dfc.t
 
 
@@ -56,8 +56,10 @@ def _w_case(x, dg, dfc, dt, dw0=None):
     dw_fc.check()
     rg, rf, ag, af = oracle_w_chunked(x, dg, dfc)
     i64 = to64(init)
-    compare("dw_g", dw_g.t.cpu(), rg + i64, dt, model_abs=sum_abs_model(ag + np.abs(i64)))
-    compare("dw_fc", dw_fc.t.cpu(), rf + 2 * i64, dt, model_abs=sum_abs_model(af + 2 * np.abs(i64)))
+    compare("dw_g", dw_g.t.cpu(), rg + i64, dt, model_abs=sum_abs_model(ag + np.abs(i64)),
+            contraction=M)
+    compare("dw_fc", dw_fc.t.cpu(), rf + 2 * i64, dt,
+            model_abs=sum_abs_model(af + 2 * np.abs(i64)), contraction=M)
     return dw_g.t, dw_fc.t
 
 
@@ -71,7 +73,7 @@ def _x_case(dg, dfc, w_g, w_fc, dt):
     torch.cuda.synchronize()
     dx.check()
     ref, a = oracle_x_rows(dg, dfc, w_g, w_fc, slice(None))
-    compare("dx", dx.t.cpu(), ref, dt, model_abs=sum_abs_model(a))
+    compare("dx", dx.t.cpu(), ref, dt, model_abs=sum_abs_model(a), contraction=2 * N)
     return dx.t
 
 
@@ -146,9 +148,12 @@ def test_gemm_stages_odd_shapes(M, K, N, dt, tile):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4, 4), (63, 36, 132), (300, 260, 268), (129, 96, 196),
-                                   (700, 256, 128), (2000, 4, 1028), (513, 1028, 76)])
+                                   (700, 256, 128), (2000, 4, 1028), (513, 1028, 76),
+                                   (2211, 896, 1504)])
 def test_gemm_stages_fp32_odd_shapes(M, K, N):
-    """The fp32 path: K and N multiples of 4, partial tiles on every side, M split or not."""
+    """The fp32 path: K and N multiples of 4, partial tiles on every side, M split or not;
+    the last shape's x stage sums 3008 products per output (the fp32 normwise bound then
+    follows the contraction length)."""
     inp = swiglu_inputs(SwiGLUShape("odd32", 14, M, K, N), dtype="fp32")
     dg, dfc = _oracle_dg(inp, "fp32")
     _w_case(inp["x"], dg, dfc, "fp32")
