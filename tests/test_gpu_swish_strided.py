@@ -3,7 +3,8 @@ the C ABI, reached from swish_grad for any non-contiguous argument) against the 
 oracle evaluated on the same logical values.  Layouts: transposed, sliced with a step,
 permuted 3-D and 5-D views, broadcast (zero-stride) inputs, a non-contiguous output whose
 gaps must stay untouched, more than 8 dimensions (merged before launch), in-place on a
-view, empty views, and a view of more than 2^32 elements (the 64-bit index path)."""
+view, empty views, a view of more than 2^32 elements (the 64-bit index path), and a
+seeded sweep of random layouts."""
 from __future__ import annotations
 
 import numpy as np
@@ -232,3 +233,68 @@ def test_more_than_2_32_elements_3d():
     _check("2^32+ broadcast 3-D", got, gs[torch.from_numpy(cols)], xs[torch.from_numpy(rows)],
            "bf16", 0.9)
 
+
+
+def _random_view(base, rng, shape):
+    """A view of ``base`` (1-D, contiguous, at least 8 x the view's elements) with logical
+    ``shape``: a random permutation of a strided slice (steps 1..3, their product at most
+    8) of a larger block."""
+    nd = len(shape)
+    steps = [1] * nd
+    for i in rng.permutation(nd):
+        st = int(rng.integers(1, 4))
+        if int(np.prod(steps)) * st <= 8:
+            steps[int(i)] = st
+    perm = [int(p) for p in rng.permutation(nd)]
+    # the block, in the permuted order, that the sliced view is cut from
+    block = [shape[perm[i]] * steps[perm[i]] for i in range(nd)]
+    t = base[:int(np.prod(block))].view(*block)
+    t = t[tuple(slice(None, None, steps[perm[i]]) for i in range(nd))]
+    inv = [perm.index(i) for i in range(nd)]
+    v = t.permute(*inv)
+    assert tuple(v.shape) == tuple(shape)
+    return v
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_strided_views(seed):
+    """Seeded random layouts: 1 to 7 dimensions, every tensor a random permutation of a
+    random step slice, inputs sometimes broadcast along a dimension, the output a view of
+    a larger buffer whose other elements must stay untouched; all three dtypes."""
+    dev = device()
+    rng = np.random.default_rng(7000 + seed)
+    dt = ["bf16", "fp16", "fp32"][seed % 3]
+    tdt = DTYPES[dt]
+    nd = int(rng.integers(1, 8))
+    shape = [int(rng.integers(1, 9 if nd > 4 else 40)) for _ in range(nd)]
+    n = int(np.prod(shape))
+    beta = [None, 1.702, 0.5, -1.3][seed % 4]
+    G, X = _values(dt, (n * 8,), 300 + seed)
+    grad = _random_view(G.to(dev), rng, shape)
+    x = _random_view(X.to(dev), rng, shape)
+    if nd > 1 and rng.random() < 0.3:        # a broadcast input along one dimension
+        d = int(rng.integers(0, nd))
+        idx = [slice(None)] * nd
+        idx[d] = slice(0, 1)
+        x = x[tuple(idx)].expand(*shape)
+    sentinel = {torch.bfloat16: 0x7FA5, torch.float16: 0x7DA5, torch.float32: 0x7FA5A5A5}[tdt]
+    ibits = torch.int32 if tdt == torch.float32 else torch.int16
+    out_base = torch.empty(n * 8, dtype=tdt, device=dev)
+    out_base.view(ibits).fill_(sentinel)
+    out = _random_view(out_base, rng, shape)
+    note(f"strided sweep {seed}: {dt} shape={shape} grad={grad.stride()} x={x.stride()} "
+         f"out={out.stride()} beta={beta}")
+    swg.swish_grad(grad, x, grad_x=out, beta=beta)
+    torch.cuda.synchronize()
+    _check("strided sweep", out, grad, x, dt, beta)
+    # every element outside the output view is untouched
+    touched = torch.zeros(n * 8, dtype=torch.int32, device=dev)
+    offs = torch.zeros(shape, dtype=torch.int64, device=dev)
+    for d_, (sz, st) in enumerate(zip(shape, out.stride())):
+        ar = torch.arange(sz, device=dev, dtype=torch.int64) * st
+        offs = offs + ar.view(*([1] * d_ + [sz] + [1] * (nd - d_ - 1)))
+    base_off = out.storage_offset() - out_base.storage_offset()
+    touched[(offs + base_off).reshape(-1)] = 1
+    rest = out_base.view(ibits)[touched == 0]
+    assert torch.all(rest == torch.tensor(sentinel, dtype=ibits, device=dev).view(ibits)), \
+        "elements outside the output view were written"
