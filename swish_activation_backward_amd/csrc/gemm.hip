@@ -44,6 +44,7 @@
 // accumulators).  Work is dealt so that concurrently running tiles with neighbouring
 // indices sit on one XCD (the hardware deals workgroup ids round-robin over the 8
 // XCDs): tiles sharing an operand panel then share that XCD's L2.
+#include <type_traits>
 #include <utility>
 
 #include "common.hpp"
@@ -311,31 +312,10 @@ template <> __device__ inline float2 unpack2<fp16>(uint32_t v) {
   return make_float2((float)h[0], (float)h[1]);
 }
 
-// Visit the accumulators of a wave as row pairs of adjacent columns: accumulator
-// registers r and r + 1 of a 32 x 32 tile are rows R and R + 1 of one column; after a
-// swap with the neighbouring lane, even lanes hold (row R, columns c, c + 1) and odd
-// lanes (row R + 1, columns c - 1, c).  fn(row, col, lo, hi) gets tile-local
-// coordinates (row, col even).
-template <int F, typename Fn>
-__device__ inline void for_each_pair(const f32x16 (&acc)[F][F], int lane_in, Fn&& fn) {
-  int lane = lane_in;
-  asm volatile("" : "+v"(lane));   // per-lane terms are formed here, not hoisted out of the
-                                   // tile loop (they would stay live, and spill)
-  const int odd = lane & 1;
-#pragma unroll
-  for (int i = 0; i < F; ++i)
-#pragma unroll
-    for (int j = 0; j < F; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
-        const float recv = swap_adjacent(odd ? v0 : v1);
-        const float lo = odd ? recv : v0, hi = odd ? v1 : recv;
-        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + odd;
-        const int col = j * 32 + ((lane & 31) & ~1);
-        fn(row, col, lo, hi);
-      }
-}
+// Row pairs of adjacent columns: accumulator registers r and r + 1 of a 32 x 32 tile are
+// rows R and R + 1 of one column; after a swap with the neighbouring lane, even lanes hold
+// (row R, columns c, c + 1) and odd lanes (row R + 1, columns c - 1, c), so that each lane
+// writes two adjacent columns of one row (the read-add-write and partial stores below).
 
 // dW[row, col] += accumulators of block row I (32 rows of the wave's WR), for a tile
 // without an M split.  `r` is a buffer window over the wave's valid dW rows (rows past K
@@ -376,6 +356,38 @@ __device__ inline void rmw_block_rows(const f32x16 (&acc)[F][F], int lane,
       __builtin_amdgcn_raw_buffer_store_b32(pack2<T>(o.x + lo, o.y + hi), r, (int)voff[j][r2],
                                             0, 0);
     }
+}
+
+// fp32 partials of block row I (32 rows of the wave's WR) straight from the accumulators:
+// after the swap with the neighbouring lane (row pairs above) each lane writes two
+// adjacent columns of one row, 8 bytes.  `r` is a buffer window over the block's valid
+// rows only, so rows past K are dropped by the range check, and so are columns past N,
+// whose offsets are pushed out of the window (cols_left: columns left from the wave's
+// first) - no branch per store.  row_bytes = 8 N < 2^25 and 32 rows keep every offset
+// below 2^30.
+template <int F, int I>
+__device__ inline void store_partial_block(const f32x16 (&acc)[F][F], int lane,
+                                           __amdgpu_buffer_rsrc_t r, uint32_t row_bytes,
+                                           int cols_left) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const int odd = lane & 1;
+  const uint32_t loff = (uint32_t)(4 * (lane >> 5) + odd) * row_bytes +
+                        (uint32_t)((lane & 31) & ~1) * 4u;
+#pragma unroll
+  for (int j = 0; j < F; ++j) {
+    const uint32_t cbad = j * 32 + ((lane & 31) & ~1) < cols_left ? 0u : kOOB;
+#pragma unroll
+    for (int r2 = 0; r2 < 8; ++r2) {
+      const int rr = 2 * r2;
+      const float v0 = acc[I][j][rr], v1 = acc[I][j][rr + 1];
+      const float recv = swap_adjacent(odd ? v0 : v1);
+      const float lo = odd ? recv : v0, hi = odd ? v1 : recv;
+      const uint32_t voff =
+          (loff + (uint32_t)(8 * (rr >> 2) + (rr & 3)) * row_bytes + 128u * j) | cbad;
+      const u32x2 v = {__float_as_uint(lo), __float_as_uint(hi)};
+      __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, 0, 0);
+    }
+  }
 }
 
 // Tile store straight from the accumulators: every lane pair turns its two rows x two
@@ -983,16 +995,30 @@ __device__ __attribute__((always_inline)) inline void w_items(
     // epilogue: rows k, columns n (of dg or dfc) straight from the accumulators
     const int64_t k0 = (int64_t)cur.k0 + wp * WR, n0 = (int64_t)cur.n0 + wq * WR;
     if (ws != nullptr) {
-      // fp32 partials in the [K, 2N] layout of split s
-      float* dst = ws + (int64_t)cur.s * K * R2 + (cur.hi ? N : 0);
-      for_each_pair(acc, lane, [&](int row, int col, float lo, float hi) {
-        const int64_t k = k0 + row, n = n0 + col;
-        if (k < K && n < N) *reinterpret_cast<float2*>(dst + k * R2 + n) = make_float2(lo, hi);
-      });
+      // fp32 partials in the [K, 2N] layout of split s, one window per 32-row block
+      float* dst = ws + (int64_t)cur.s * K * R2 + (cur.hi ? N : 0) + n0;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));   // lane terms formed here: hoisted out of the tile
+                                     // loop they would stay live, and spill
+      const uint32_t row_bytes = (uint32_t)(R2 * 4);
+      const int cols_left = (int)(N - n0);
+      auto block = [&](auto I) {
+        constexpr int i = decltype(I)::value;
+        const int64_t kb = k0 + 32 * i;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(dst + kb * R2, clamp_bytes(K - kb < 32 ? K - kb : 32, R2 * 4));
+        store_partial_block<F, i>(acc, ln, r, row_bytes, cols_left);
+      };
+      block(std::integral_constant<int, 0>{});
+      block(std::integral_constant<int, 1>{});
+      if constexpr (F == 4) {
+        block(std::integral_constant<int, 2>{});
+        block(std::integral_constant<int, 3>{});
+      }
     } else {
       T* dw = cur.hi ? dwfc : dwg;
       int ln = lane;
-      asm volatile("" : "+v"(ln));   // lane terms formed here, not hoisted (see for_each_pair)
+      asm volatile("" : "+v"(ln));   // lane terms formed here: hoisted out of the tile
+                                     // loop they would stay live, and spill
       const int64_t krows = K - k0 < WR ? K - k0 : WR;
       const __amdgpu_buffer_rsrc_t r = make_rsrc(dw + k0 * N + n0, clamp_bytes(krows, N * 2));
       const uint32_t row_bytes = (uint32_t)(N * 2);
@@ -1130,13 +1156,16 @@ __device__ inline void f_read(const uint16_t* slot, int wp, int lane, const int 
 // nt): g, fc and y, 1.35 GB at the large-batch shape, are not read again by this kernel,
 // and keeping them out of the caches leaves the x and W panels there (forward 679-683 ->
 // 629-632 us in a same-board comparison; the x stage's dx stores gained nothing from it).
+// Unconditional: columns past N carry offsets outside the window (the caller ORs in
+// kOOB), which the range check drops; a per-lane branch around each store (three per
+// element pair, exec-mask save and restore each) cost 602-612 against 557-572 us.
 template <typename T>
 __device__ inline void f_store_pair(float v0, float v1, uint32_t sel, __amdgpu_buffer_rsrc_t r,
-                                    uint32_t voff, bool ok) {
+                                    uint32_t voff) {
   const uint32_t own = pack2<T>(v0, v1);
   const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);
   const uint32_t out = __builtin_amdgcn_perm(nb, own, sel);
-  if (ok) __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)voff, 0, 2);
+  __builtin_amdgcn_raw_buffer_store_b32(out, r, (int)voff, 0, 2);
 }
 
 // One forward issue: the tile's x window with the stage's first column as soffset, the
@@ -1344,7 +1373,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       for (int jj = 0; jj < 2; ++jj) {
         const int colv = wq * 64 + jj * 32 + (ln & 31);          // this lane's column
         const int colp = wq * 64 + jj * 32 + ((ln & 31) & ~1);   // its pair's first column
-        const bool okc = colp < nleft;
+        // columns past N: offsets pushed out of the window, dropped by the range check
+        uint32_t cbad = colp < nleft ? 0u : kOOB;
+        asm volatile("" : "+v"(cbad));
         const float bgv = (bg != nullptr && colv < nleft) ? to_f32(bg[cur.n0 + colv]) : 0.0f;
         const float bfv = (bfc != nullptr && colv < nleft) ? to_f32(bfc[cur.n0 + colv]) : 0.0f;
         const uint32_t loff = (uint32_t)(4 * (ln >> 5) + odd) * row_bytes + (uint32_t)colp * 2u;
@@ -1353,13 +1384,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
           for (int rr = 0; rr < 16; rr += 2) {
             const uint32_t voff =
-                loff + (uint32_t)(wp * 128 + i * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes;
+                (loff + (uint32_t)(wp * 128 + i * 32 + 8 * (rr >> 2) + (rr & 3)) * row_bytes) | cbad;
             const float g0 = acc[i][jj][rr] + bgv, g1 = acc[i][jj][rr + 1] + bgv;
             const float c0 = acc[i][2 + jj][rr] + bfv, c1 = acc[i][2 + jj][rr + 1] + bfv;
             const float s0 = sigmoid_only(g0), s1 = sigmoid_only(g1);
-            f_store_pair<T>(g0, g1, sel, rgo, voff, okc);
-            f_store_pair<T>(c0, c1, sel, rfo, voff, okc);
-            f_store_pair<T>(g0 * s0 * c0, g1 * s1 * c1, sel, ryo, voff, okc);
+            f_store_pair<T>(g0, g1, sel, rgo, voff);
+            f_store_pair<T>(c0, c1, sel, rfo, voff);
+            f_store_pair<T>(g0 * s0 * c0, g1 * s1 * c1, sel, ryo, voff);
           }
       }
     }
