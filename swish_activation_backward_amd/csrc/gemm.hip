@@ -1343,6 +1343,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   for (int64_t j = 0; j < my_tiles; ++j) {
     const FTile nxt = f_tile(f0 + (j + 1) * G, j + 1 < my_tiles, nn);
     zero_acc(acc);
+    // the cleared accumulators pinned in AGPRs here: otherwise the register allocator
+    // gives the loop's first steps another AGPR set and copies between them (192 moves
+    // per tile; 584 -> 555 us without them, same bits)
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+#pragma unroll
+      for (int q = 0; q < FQ; ++q) asm volatile("" : "+a"(acc[i][q]));
     F_READ(ring, frags[0]);
     int64_t t = 0;
     for (; t + 4 < nst; t += 4) {
