@@ -32,8 +32,11 @@
  *     code is then available from swg_last_hip_error().  Calls whose work is empty return
  *     SWG_OK without launching anything.
  *   - Calls are thread-safe: the library keeps no state apart from the last HIP error, the
- *     timing events of swg_time_next_call (both per host thread) and the device scratch
- *     of swiglu_bwd_b_noalloc.
+ *     timing events of swg_time_next_call and the tile setting of swg_set_gemm_tile (all
+ *     per host thread), the cached compute-unit count of each device and the device
+ *     scratch of swiglu_bwd_b_noalloc.
+ *   - A workspace is in use until the call's kernels have finished on its stream: calls
+ *     that may run at the same time (on different streams) need distinct workspaces.
  */
 #ifndef SWIGLU_BWD_H
 #define SWIGLU_BWD_H
