@@ -45,6 +45,44 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), f"{n} declared in include/swiglu_bwd.h but not exported"
 
 
+def test_header_is_plain_c_and_links(lib, tmp_path):
+    """A C99 program (gcc -std=c99 -pedantic -Werror) includes the header, takes the address
+    of every declared function, links against the in-tree library and runs its host-only
+    calls: the boundary needs neither C++ nor torch."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not installed")
+    names = declared_functions()
+    libdir = os.path.dirname(swg.library_path())
+    src = tmp_path / "main.c"
+    src.write_text(
+        "#include <stdio.h>\n#include \"swiglu_bwd.h\"\n"
+        "static void (*const table[])(void) = {\n"
+        + "".join(f"  (void (*)(void)){n},\n" for n in names)
+        + "};\n"
+        "int main(void) {\n"
+        "  printf(\"%d\\n\", (int)(sizeof(table) / sizeof(table[0])));\n"
+        "  printf(\"%s\\n\", swg_version());\n"
+        "  printf(\"%zu\\n\", swiglu_bwd_b_workspace_size(220000, 1024, SWG_BF16));\n"
+        "  printf(\"%d\\n\", swiglu_bwd_gemm_tile(1, 8191, 512, 1024, SWG_BF16));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "main"
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+           "-L", libdir, "-lswiglu_bwd", f"-Wl,-rpath,{libdir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr[-2000:]
+    lines = out.stdout.splitlines()
+    assert int(lines[0]) == len(names)
+    assert lines[1].startswith("swiglu_bwd ") and lines[1].endswith("gfx950")
+    assert int(lines[2]) == lib.swiglu_bwd_b_workspace_size(220000, 1024, BF16)
+    assert int(lines[3]) == 128   # the 128 x 128 x-stage tile at the ragged batch
+
+
 def test_status_strings_and_version(lib):
     for code in range(6):
         s = lib.swg_status_string(code).decode()
